@@ -1,0 +1,253 @@
+"""Seeded synthetic inputs for the H3-style DiT forward.
+
+This module only produces numbers: weights, activations, modulation tables,
+rotary tables and tile maps drawn from a counter-based generator (SplitMix64 +
+Box-Muller, defined in ``synth.c``).  It holds none of the forward's
+arithmetic.  The CPU oracle and the GPU path are both fed from here, so they
+see the same bytes.
+
+bf16 tensors are returned as ``numpy.uint16`` arrays of raw bf16 bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libh3synth.so")
+_lib = None
+
+SEED = 42
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from audio_diffusion_transformer_amd import build as _build
+        _build.build_synth()
+    lib = ctypes.CDLL(_LIB_PATH)
+    u64, i64, dbl, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.synth_key.argtypes = [u64, u64]
+    lib.synth_key.restype = u64
+    lib.synth_uniform_f64.argtypes = [u64, u64, u64, i64, vp]
+    lib.synth_normal_f64.argtypes = [u64, u64, u64, i64, vp]
+    lib.synth_normal_bf16.argtypes = [u64, u64, u64, i64, dbl, dbl, vp]
+    lib.synth_uniform_f32.argtypes = [u64, u64, u64, i64, dbl, dbl, vp]
+    lib.synth_f32_to_bf16.argtypes = [vp, i64, vp]
+    for f in (lib.synth_uniform_f64, lib.synth_normal_f64, lib.synth_normal_bf16,
+              lib.synth_uniform_f32, lib.synth_f32_to_bf16):
+        f.restype = None
+    _lib = lib
+    return lib
+
+
+def stream_id(name: str) -> int:
+    """FNV-1a 64-bit hash of a tensor's name: the generator's stream number."""
+    h = 0xCBF29CE484222325
+    for b in name.encode():
+        h ^= b
+        h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def normal_bf16(name, shape, std, mean=0.0, seed=SEED, out=None):
+    n = int(np.prod(shape))
+    if out is None:
+        out = np.empty(shape, dtype=np.uint16)
+    assert out.dtype == np.uint16 and out.flags.c_contiguous and out.size == n
+    _load().synth_normal_bf16(seed, stream_id(name), 0, n, float(mean), float(std),
+                              out.ctypes.data)
+    return out
+
+
+def uniform_f32(name, shape, lo, hi, seed=SEED):
+    n = int(np.prod(shape))
+    out = np.empty(shape, dtype=np.float32)
+    _load().synth_uniform_f32(seed, stream_id(name), 0, n, float(lo), float(hi),
+                              out.ctypes.data)
+    return out
+
+
+def normal_f64(name, shape, seed=SEED):
+    n = int(np.prod(shape))
+    out = np.empty(shape, dtype=np.float64)
+    _load().synth_normal_f64(seed, stream_id(name), 0, n, out.ctypes.data)
+    return out
+
+
+def uniform_f64(name, shape, seed=SEED):
+    n = int(np.prod(shape))
+    out = np.empty(shape, dtype=np.float64)
+    _load().synth_uniform_f64(seed, stream_id(name), 0, n, out.ctypes.data)
+    return out
+
+
+def f32_to_bf16(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().synth_f32_to_bf16(a.ctypes.data, a.size, out.ctypes.data)
+    return out
+
+
+def bf16_bits_to_f32(u):
+    """Exact widening of raw bf16 bits to float32 (a storage-format view)."""
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Workload shapes
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    n_text: int
+    n_audio: int
+    n_video: int
+    hidden: int
+    n_heads: int
+    head_dim: int
+    ffn: int
+    tile: int = 64
+    top_k: int = 4
+    pooled: int = 1
+    norm_eps: float = 1e-6
+    c_video: int = 96
+    c_audio: int = 32
+
+    @property
+    def rows(self):
+        return self.n_text + self.n_audio + self.n_video
+
+    @property
+    def n_prefix(self):
+        return self.n_text + self.n_audio
+
+    def replace(self, **kw):
+        return dataclasses.replace(self, **kw)
+
+
+# The three single-block shapes: tiny, mid and full scale.
+TINY = Shape(64, 64, 896, 256, 4, 64, 1024, tile=64, top_k=4)
+MID = Shape(256, 256, 4096, 3072, 24, 128, 12288, tile=64, top_k=16)
+FULL = Shape(512, 543, 14380, 5120, 40, 128, 20480, tile=64, top_k=32)
+CONFIGS = {"tiny": TINY, "mid": MID, "full": FULL}
+
+
+def tile_map(shape: Shape):
+    """Contiguous runs of ``shape.tile`` rows per segment, ragged last tile.
+
+    Returns (tile_start int32 [n_tiles+1], n_prefix_tiles).
+    """
+    starts = []
+    r = 0
+    n_prefix_tiles = 0
+    for seg_i, n in enumerate((shape.n_text, shape.n_audio, shape.n_video)):
+        for s in range(0, n, shape.tile):
+            starts.append(r + s)
+            if seg_i < 2:
+                n_prefix_tiles += 1
+        r += n
+    starts.append(r)
+    return np.asarray(starts, dtype=np.int32), n_prefix_tiles
+
+
+def rope_tables(shape: Shape):
+    """fp32 [R][d/2][2] (cos, sin); position = row index within its segment,
+    angle_i = pos * 10000^(-2i/d)."""
+    d2 = shape.head_dim // 2
+    pos = np.concatenate([np.arange(shape.n_text), np.arange(shape.n_audio),
+                          np.arange(shape.n_video)]).astype(np.float64)
+    inv = 10000.0 ** (-2.0 * np.arange(d2, dtype=np.float64) / shape.head_dim)
+    ang = pos[:, None] * inv[None, :]
+    out = np.empty((shape.rows, d2, 2), dtype=np.float32)
+    out[..., 0] = np.cos(ang)
+    out[..., 1] = np.sin(ang)
+    return out
+
+
+def block_weights(shape: Shape, block: int = 0, seed: int = SEED, std: float = 0.02):
+    H, F, d = shape.hidden, shape.ffn, shape.head_dim
+    p = f"block{block}."
+    w = {
+        "w_qkv": normal_bf16(p + "w_qkv", (3 * H, H), std, seed=seed),
+        "b_qkv": normal_bf16(p + "b_qkv", (3 * H,), std, seed=seed),
+        "q_gain": normal_bf16(p + "q_gain", (d,), std, mean=1.0, seed=seed),
+        "k_gain": normal_bf16(p + "k_gain", (d,), std, mean=1.0, seed=seed),
+        "w_o": normal_bf16(p + "w_o", (H, H), std, seed=seed),
+        "b_o": normal_bf16(p + "b_o", (H,), std, seed=seed),
+        "w_fc1": normal_bf16(p + "w_fc1", (F, H), std, seed=seed),
+        "b_fc1": normal_bf16(p + "b_fc1", (F,), std, seed=seed),
+        "w_fc2": normal_bf16(p + "w_fc2", (H, F), std, seed=seed),
+        "b_fc2": normal_bf16(p + "b_fc2", (H,), std, seed=seed),
+    }
+    return w
+
+
+def head_weights(shape: Shape, seed: int = SEED, std: float = 0.02):
+    H = shape.hidden
+    return {
+        "w_video": normal_bf16("head.w_video", (shape.c_video, H), std, seed=seed),
+        "b_video": normal_bf16("head.b_video", (shape.c_video,), std, seed=seed),
+        "w_audio": normal_bf16("head.w_audio", (shape.c_audio, H), std, seed=seed),
+        "b_audio": normal_bf16("head.b_audio", (shape.c_audio,), std, seed=seed),
+    }
+
+
+def modulation(shape: Shape, block: int = 0, step: int = 0, seed: int = SEED, amp=0.1):
+    """fp32 [3 segments][6][H]: (shift1, scale1, gate1, shift2, scale2, gate2)."""
+    return uniform_f32(f"mod.step{step}.block{block}", (3, 6, shape.hidden), -amp, amp,
+                       seed=seed)
+
+
+def final_modulation(shape: Shape, step: int = 0, seed: int = SEED, amp=0.1):
+    """fp32 [3 segments][2][H]: (shift, scale) of the final norm."""
+    return uniform_f32(f"mod_final.step{step}", (3, 2, shape.hidden), -amp, amp, seed=seed)
+
+
+def lowrank_field(n_rows: int, rank: int = 4, seed: int = SEED, name="field"):
+    """phi_j(p) = sin(2 pi f_j p / n + theta_j), f = (1, 3, 7, 17, ...): [n_rows][rank]."""
+    freqs = np.asarray([1, 3, 7, 17, 31, 59][:rank], dtype=np.float64)
+    theta = 2 * math.pi * uniform_f64(name + ".theta", (rank,), seed=seed)
+    p = np.arange(n_rows, dtype=np.float64)
+    return np.sin(2 * math.pi * freqs[None, :] * p[:, None] / max(n_rows, 1) + theta[None, :])
+
+
+def activations(shape: Shape, seed: int = SEED, field: bool = False, name="x_in"):
+    """x_in bf16 [R][H] ~ N(0, 1).  With ``field``, video rows also carry a
+    rank-4 smooth spatial field phi(p) @ B, B ~ N(0,1)^{4 x H}, so tile means
+    differ across tiles and the top-k choice has clear margins."""
+    x = normal_bf16(name, (shape.rows, shape.hidden), 1.0, seed=seed)
+    if not field:
+        return x
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    phi = lowrank_field(shape.n_video, 4, seed=seed, name=name + ".phi")
+    basis = normal_f64(name + ".basis", (4, shape.hidden), seed=seed)
+    xf[shape.n_prefix:] += phi @ basis
+    return f32_to_bf16(xf.astype(np.float32))
+
+
+def attn_qkv(shape: Shape, seed: int = SEED, correlated: bool = True, amp: float = 1.0):
+    """q, k, v bf16 [nh][R][d] ~ N(0, 1); with ``correlated``, video rows of q
+    and k get a rank-4 field phi(p) @ A_h (resp. B_h), A_h, B_h ~ N(0,1)^{4 x d}."""
+    nh, R, d = shape.n_heads, shape.rows, shape.head_dim
+    q = normal_bf16("attn.q", (nh, R, d), 1.0, seed=seed)
+    k = normal_bf16("attn.k", (nh, R, d), 1.0, seed=seed)
+    v = normal_bf16("attn.v", (nh, R, d), 1.0, seed=seed)
+    if not correlated:
+        return q, k, v
+    phi = lowrank_field(shape.n_video, 4, seed=seed, name="attn.phi")
+    A = normal_f64("attn.A", (nh, 4, d), seed=seed)
+    B = normal_f64("attn.B", (nh, 4, d), seed=seed)
+    P = shape.n_prefix
+    qf = bf16_bits_to_f32(q)
+    kf = bf16_bits_to_f32(k)
+    for h in range(nh):
+        qf[h, P:] += (amp * (phi @ A[h])).astype(np.float32)
+        kf[h, P:] += (amp * (phi @ B[h])).astype(np.float32)
+    return f32_to_bf16(qf), f32_to_bf16(kf), v

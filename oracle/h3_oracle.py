@@ -1,0 +1,384 @@
+"""CPU oracle for the H3-style joint video+audio DiT forward.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module; the product path never does.  It
+shares no code with the HIP library.
+
+What it computes, and where each step comes from:
+
+* "Antirez/h3.c: MiniMax H3 inference engine for Mac computers" (the h3.c
+  README, implementation notes): fused gated AdaLN with a rounded bf16
+  residual, QKV rows interleaved per attention head, fused Q/K RMS norm and
+  RoPE, bf16 output heads, F32 rows out.
+* "TensorFold PR #949" (FastH3 DiT forward on Zig + Metal): sections
+  "Precision is the checkpoint's own" (bf16 weights and activations, fp32
+  sums, fp32 tile means / scores / top-k / pooled branch, softmax weights
+  rounded to bf16 before the value product), "What it adds" (block.zig:
+  modulated norm, q/k/v products, head layout with q/k norm and rotary, tile
+  means, tile scores, top-k, pooled branch, tile-routed attention with an
+  online softmax, out projection, MLP), and "Kernel contract" (top-k rule:
+  a NaN score ranks as -inf, ties go to the lower tile).
+
+Arithmetic: every value is carried in float64.  Rounding happens only where
+the pages put it: bf16 (round to nearest even) at the activation storage
+points, fp32 for the tile means and tile scores, whose fp32 values decide the
+top-k.  Matrix products use numpy's matmul (a library primitive) in float64.
+
+Readings where the pages are silent (each listed with its reason in the
+design notes): RMS norm without a learned gain, eps 1e-6; modulation as
+(1 + scale) and + shift, one set of six vectors per segment (text, audio,
+video); gate as x + g * branch; GELU with exact erf; biases on every linear;
+half-split RoPE pairs (i, i + d/2) from caller tables; scale d^-1/2 on row and
+tile scores; prefix (text + audio) keys always attended by video rows, top-k
+over video key tiles only; tile-mean divisor = true row count; pooled branch =
+softmax over all key tiles of the tile scores times the key tiles' value means,
+added in full precision before the bf16 rounding of the attention output; text
+and audio rows attend densely with no pooled term; softmax denominator uses the
+unrounded weights.
+
+Parity against a released H3 / FastH3 checkpoint is unpinned (no weights,
+case file or reference velocities are available); every function here is
+pinned by the tests in tests/test_oracle_*.py against closed forms,
+invariants, library routines and brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erf as _erf
+
+TEXT, AUDIO, VIDEO = 0, 1, 2
+
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+
+def bf16_to_f64(u16):
+    """Raw bf16 bits -> float64 (exact)."""
+    u = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x):
+    """float64 -> nearest bf16 value (ties to even), returned as float64.
+
+    bf16 = 1 sign, 8 exponent, 7 fraction bits (fp32's exponent range).
+    Normal range: keep the top 7 of the 52 fraction bits of the float64,
+    rounding the dropped 45 bits to nearest, ties to even.  Below 2^-126
+    (bf16 subnormals) the grid is uniform with step 2^-133.  Results beyond
+    the largest finite bf16 become +-inf; NaN stays NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    fin = np.isfinite(x)
+    small = fin & (np.abs(x) < 2.0 ** -126)
+    norm = fin & ~small
+    bits = x[norm].view(np.uint64)
+    half = np.uint64(1) << np.uint64(44)
+    lsb = (bits >> np.uint64(45)) & np.uint64(1)
+    bits = (bits + (half - np.uint64(1)) + lsb) & ~((np.uint64(1) << np.uint64(45)) - np.uint64(1))
+    r = bits.view(np.float64)
+    bf16_max = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r = np.where(np.abs(r) > bf16_max, np.copysign(np.inf, r), r)
+    out[norm] = r
+    step = 2.0 ** -133
+    out[small] = np.round(x[small] / step) * step   # np.round: half to even
+    out[~fin] = x[~fin]
+    return out
+
+
+def f64_to_bf16_bits(x):
+    """float64 values that are exactly bf16 -> raw bits (uint16)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def round_f32(x):
+    """float64 -> nearest float32 (numpy's cast rounds to nearest even), as float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Rows, segments, tiles
+# ----------------------------------------------------------------------------
+
+def row_segments(n_text, n_audio, n_video):
+    """Segment id of every packed row: text rows, then audio, then video
+    (one packed sequence; TensorFold PR #949, opening summary)."""
+    return np.concatenate([np.full(n_text, TEXT), np.full(n_audio, AUDIO),
+                           np.full(n_video, VIDEO)]).astype(np.int64)
+
+
+def check_tile_map(tile_start, n_text, n_audio, n_video, n_prefix_tiles):
+    ts = np.asarray(tile_start, dtype=np.int64)
+    R = n_text + n_audio + n_video
+    assert ts[0] == 0 and ts[-1] == R and np.all(np.diff(ts) > 0)
+    assert ts[n_prefix_tiles] == n_text + n_audio
+    return ts
+
+
+# ----------------------------------------------------------------------------
+# Block pieces
+# ----------------------------------------------------------------------------
+
+def modulated_rmsnorm(x, shift, scale, seg, eps):
+    """Modulated norm (AdaLN): bf( x * (mean_k x_k^2 + eps)^-1/2 * (1 + scale[seg]) + shift[seg] ).
+
+    x: float64 [n][H] (bf16 values); shift, scale: [3][H] per segment; seg:
+    the segment id of each of the n rows.
+    h3.c README (fused gated AdaLN notes: per-row RMS, rounded bf16 output);
+    TensorFold PR #949, "What it adds" (modulated norm)."""
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    y = x * (ms + eps) ** -0.5 * (1.0 + scale[seg]) + shift[seg]
+    return round_bf16(y)
+
+
+def linear(a, w, b):
+    """a @ w^T + b in float64 (weights stored [out][in])."""
+    return a @ w.T + b
+
+
+def gelu(z):
+    """GELU with the exact normal CDF: 0.5 z (1 + erf(z / sqrt 2))."""
+    return 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
+
+
+def split_qkv(y, n_heads, head_dim):
+    """Per-head interleaved projection rows [h][q|k|v][d] (h3.c README, note on
+    the checkpoint's QKV layout) -> q, k, v as [nh][R][d]."""
+    R = y.shape[0]
+    t = y.reshape(R, n_heads, 3, head_dim)
+    q = np.ascontiguousarray(t[:, :, 0, :].transpose(1, 0, 2))
+    k = np.ascontiguousarray(t[:, :, 1, :].transpose(1, 0, 2))
+    v = np.ascontiguousarray(t[:, :, 2, :].transpose(1, 0, 2))
+    return q, k, v
+
+
+def qk_norm_rope(u, gain, rope, eps):
+    """Per-head RMS norm with gain, then rotary embedding, then bf16.
+
+    u: [nh][R][d] (bf16 values); gain: [d]; rope: fp32 [R][d/2][2] (cos, sin)
+    or None (identity).  Pairs are (i, i + d/2):
+    (a, b) -> (a cos - b sin, b cos + a sin).
+    TensorFold PR #949, "What it adds" (head layout with q/k norm and rotary);
+    h3.c README (fused Q/K normalization and RoPE)."""
+    d = u.shape[-1]
+    ms = np.mean(u * u, axis=-1, keepdims=True)
+    t = u * (ms + eps) ** -0.5 * gain
+    if rope is None:
+        return round_bf16(t)
+    c = rope[None, :, :, 0].astype(np.float64)
+    s = rope[None, :, :, 1].astype(np.float64)
+    a, b = t[..., : d // 2], t[..., d // 2:]
+    return round_bf16(np.concatenate([a * c - b * s, b * c + a * s], axis=-1))
+
+
+def tile_means(u, tile_start, tiles):
+    """fp32 mean over each listed tile's rows: [nh][len(tiles)][d]
+    (TensorFold PR #949, "Precision": fp32 tile means).  Divisor: the tile's
+    true row count."""
+    out = np.empty((u.shape[0], len(tiles), u.shape[2]))
+    for j, t in enumerate(tiles):
+        s, e = tile_start[t], tile_start[t + 1]
+        out[:, j, :] = np.sum(u[:, s:e, :], axis=1) / (e - s)
+    return round_f32(out)
+
+
+def tile_scores(qbar, kbar):
+    """fp32 tile scores S[h][i][j] = (qbar_i . kbar_j) * d^-1/2 (TensorFold PR
+    #949, "What it adds": tile scores; "Precision": fp32 scores)."""
+    d = qbar.shape[-1]
+    return round_f32(np.einsum("hid,hjd->hij", qbar, kbar) * d ** -0.5)
+
+
+def topk_tiles(scores_row, cand, k):
+    """The k candidate tiles with the largest score, returned ascending.
+
+    Rule from TensorFold PR #949, "Kernel contract": a NaN score ranks as
+    -inf and ties go to the lower tile.  k >= len(cand) keeps all of them."""
+    cand = np.asarray(cand)
+    if k >= len(cand):
+        return np.sort(cand)
+    s = np.where(np.isnan(scores_row[cand]), -np.inf, scores_row[cand])
+    order = np.lexsort((cand, -s))          # primary: larger score; then lower index
+    return np.sort(cand[order[:k]])
+
+
+def pooled_branch(scores_row, vbar):
+    """Pooled (coarse) branch for one query tile: softmax over all key tiles
+    of the tile scores, times the key tiles' value means (TensorFold PR #949,
+    "What it adds": the pooled branch over tile means)."""
+    m = np.max(scores_row)
+    w = np.exp(scores_row - m)
+    return (w @ vbar) / np.sum(w)
+
+
+def softmax_rows_bf16p(q, kk, vv):
+    """Attention of query rows q [n][d] over keys kk/vv [m][d].
+
+    Scores are scaled by d^-1/2; p = exp(s - max s); the value product uses
+    p rounded to bf16, the denominator the unrounded sum (TensorFold PR #949,
+    "Precision": softmax weights rounded to bf16 before the value product)."""
+    d = q.shape[-1]
+    s = (q @ kk.T) * d ** -0.5
+    m = np.max(s, axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = np.sum(p, axis=1, keepdims=True)
+    return (round_bf16(p) @ vv) / l
+
+
+def routing(q, k, v, tile_start, n_prefix_tiles, top_k):
+    """Tile means, tile scores, top-k video key tiles and the pooled branch.
+
+    q, k, v: [nh][R][d] float64 (bf16 values).  Returns dict with
+    qbar [nh][nQ][d], kbar, vbar [nh][nK][d], scores [nh][nQ][nK] (fp32
+    values), sel [nh][nQ][min(k, nQ)] (absolute tile ids), pooled
+    [nh][nQ][d]."""
+    nK = len(tile_start) - 1
+    vid_tiles = list(range(n_prefix_tiles, nK))
+    qbar = tile_means(q, tile_start, vid_tiles)
+    kbar = tile_means(k, tile_start, range(nK))
+    vbar = tile_means(v, tile_start, range(nK))
+    S = tile_scores(qbar, kbar)
+    nh, nQ = S.shape[0], S.shape[1]
+    kk = min(top_k, nQ)
+    sel = np.empty((nh, nQ, kk), dtype=np.int64)
+    pooled = np.empty((nh, nQ, q.shape[-1]))
+    for h in range(nh):
+        for i in range(nQ):
+            sel[h, i] = topk_tiles(S[h, i], np.asarray(vid_tiles), top_k)
+            pooled[h, i] = pooled_branch(S[h, i], vbar[h])
+    return dict(qbar=qbar, kbar=kbar, vbar=vbar, scores=S, sel=sel, pooled=pooled)
+
+
+def attention(q, k, v, tile_start, n_prefix_tiles, n_prefix_rows, rt, use_pooled,
+              rows=None, gate=None):
+    """Attention output, row-major [len(rows)][nh*d] (float64 before the bf16
+    rounding is applied by the caller via round_bf16).
+
+    Text and audio rows attend densely over all rows (TensorFold PR #949,
+    parity notes: the audio rows' attention is dense).  A video row in query
+    tile i attends the prefix rows, then the rows of the tiles in sel[h][i] in
+    ascending order; with the pooled branch on, pooled[h][i] (times the gate,
+    if one is given) is added before rounding."""
+    nh, R, d = q.shape
+    if rows is None:
+        rows = np.arange(R)
+    rows = np.asarray(rows)
+    out = np.zeros((len(rows), nh * d))
+    nK = len(tile_start) - 1
+    tile_of = np.searchsorted(tile_start, np.arange(R), side="right") - 1
+    dense_idx = np.nonzero(rows < n_prefix_rows)[0]
+    vid_idx = np.nonzero(rows >= n_prefix_rows)[0]
+    for h in range(nh):
+        if len(dense_idx):
+            rr = rows[dense_idx]
+            out[dense_idx, h * d:(h + 1) * d] = softmax_rows_bf16p(q[h, rr], k[h], v[h])
+        if len(vid_idx):
+            rr = rows[vid_idx]
+            tiles = tile_of[rr]
+            for t in np.unique(tiles):
+                i = t - n_prefix_tiles
+                sel_rows = [np.arange(tile_start[j], tile_start[j + 1]) for j in rt["sel"][h, i]]
+                keys = np.concatenate([np.arange(n_prefix_rows)] + sel_rows)
+                m = tiles == t
+                o = softmax_rows_bf16p(q[h, rr[m]], k[h, keys], v[h, keys])
+                if use_pooled:
+                    pb = rt["pooled"][h, i]
+                    if gate is not None:
+                        o = o + gate[h, rr[m]] * pb
+                    else:
+                        o = o + pb
+                out[vid_idx[m], h * d:(h + 1) * d] = o
+    return out
+
+
+def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=None):
+    """One DiT block, steps in the order of TensorFold PR #949 "What it adds"
+    (block.zig) with the GELU MLP of the workload description:
+
+      n1 = modnorm(x; shift1, scale1)
+      y  = bf(n1 Wqkv^T + b); q, k, v per head; q~, k~ = bf(rope(rmsnorm(.)*gain))
+      routing on q~, k~, v (tile means, scores, top-k, pooled)
+      a  = bf(attention)
+      o  = bf(a Wo^T + bo);            x1 = bf(x + gate1 * o)
+      n2 = modnorm(x1; shift2, scale2)
+      h  = bf(gelu(n2 W1^T + b1));     f = bf(h W2^T + b2);   x2 = bf(x1 + gate2 * f)
+
+    sh: object with n_text, n_audio, n_video, n_heads, head_dim, norm_eps,
+    top_k, pooled.  w: dict of bf16-bit arrays (see synth.block_weights).
+    mod: fp32 [3][6][H].  rope: fp32 [R][d/2][2] or None.  x_in: bf16 bits.
+    out_rows: None for all rows, else the rows whose attention / x1 / x2 are
+    computed (q, k, v and routing always cover all rows).
+    Returns a dict of float64 intermediates (bf16 values where rounded)."""
+    seg = row_segments(sh.n_text, sh.n_audio, sh.n_video)
+    P = sh.n_text + sh.n_audio
+    ts = check_tile_map(tile_start, sh.n_text, sh.n_audio, sh.n_video, n_prefix_tiles)
+    x = bf16_to_f64(x_in)
+    mod = np.asarray(mod, dtype=np.float64)
+    shift1, scale1, gate1, shift2, scale2, gate2 = (mod[:, i, :] for i in range(6))
+    eps = sh.norm_eps
+    f = {k_: bf16_to_f64(v_) for k_, v_ in w.items()}
+
+    n1 = modulated_rmsnorm(x, shift1, scale1, seg, eps)
+    y = round_bf16(linear(n1, f["w_qkv"], f["b_qkv"]))
+    q, k, v = split_qkv(y, sh.n_heads, sh.head_dim)
+    qt = qk_norm_rope(q, f["q_gain"], rope, eps)
+    kt = qk_norm_rope(k, f["k_gain"], rope, eps)
+    rt = routing(qt, kt, v, ts, n_prefix_tiles, sh.top_k)
+    rows = np.arange(x.shape[0]) if out_rows is None else np.asarray(out_rows)
+    a = round_bf16(attention(qt, kt, v, ts, n_prefix_tiles, P, rt, bool(sh.pooled), rows))
+    sr = seg[rows]
+    o = round_bf16(linear(a, f["w_o"], f["b_o"]))
+    x1 = round_bf16(x[rows] + gate1[sr] * o)
+    n2 = modulated_rmsnorm(x1, shift2, scale2, sr, eps)
+    hdn = round_bf16(gelu(linear(n2, f["w_fc1"], f["b_fc1"])))
+    ff = round_bf16(linear(hdn, f["w_fc2"], f["b_fc2"]))
+    x2 = round_bf16(x1 + gate2[sr] * ff)
+    return dict(rows=rows, n1=n1, y=y, q=qt, k=kt, v=v, attn=a, o=o, x1=x1, n2=n2, h=hdn,
+                f=ff, x2=x2, **rt)
+
+
+def final_heads(sh, x, mod_final, head):
+    """Final modulated norm on audio and video rows, then the narrow output
+    heads, F32 out with no rounding (h3.c README: final audio/video AdaLN and
+    bf16 heads; TensorFold PR #949, "What it adds": rows out as raw f32).
+
+    x: float64 [R][H]; mod_final fp32 [3][2][H] (shift, scale); head: dict of
+    bf16 bits w_video [cv][H], b_video, w_audio [ca][H], b_audio."""
+    seg = row_segments(sh.n_text, sh.n_audio, sh.n_video)
+    mf = np.asarray(mod_final, dtype=np.float64)
+    z = modulated_rmsnorm(x, mf[:, 0, :], mf[:, 1, :], seg, sh.norm_eps)
+    P = sh.n_text + sh.n_audio
+    za = z[sh.n_text:P]
+    zv = z[P:]
+    vel_video = linear(zv, bf16_to_f64(head["w_video"]), bf16_to_f64(head["b_video"]))
+    vel_audio = linear(za, bf16_to_f64(head["w_audio"]), bf16_to_f64(head["b_audio"]))
+    return vel_video, vel_audio
+
+
+def dit_forward(sh, tile_start, n_prefix_tiles, blocks, head, mods, mod_final, rope, x_in):
+    """L blocks, then the final norm and heads (TensorFold PR #949 opening
+    summary: 50 blocks denoise one packed sequence).  blocks: list of weight
+    dicts; mods: [L][3][6][H]."""
+    x_bits = np.asarray(x_in, dtype=np.uint16)
+    x = bf16_to_f64(x_bits)
+    for l, w in enumerate(blocks):
+        r = block_forward(sh, tile_start, n_prefix_tiles, w, mods[l], rope, x_bits)
+        x = r["x2"]
+        x_bits = f64_to_bf16_bits(x)
+    vv, va = final_heads(sh, x, mod_final, head)
+    return dict(x=x, vel_video=vv, vel_audio=va)
+
+
+def routed_attn(sh, tile_start, n_prefix_tiles, q_bits, k_bits, v_bits, rows=None, gate=None):
+    """Stand-alone routed attention on given head-major q, k, v (bf16 bits,
+    [nh][R][d]): routing then attention, output bf16 values [rows][nh*d]."""
+    q, k, v = bf16_to_f64(q_bits), bf16_to_f64(k_bits), bf16_to_f64(v_bits)
+    ts = check_tile_map(tile_start, sh.n_text, sh.n_audio, sh.n_video, n_prefix_tiles)
+    rt = routing(q, k, v, ts, n_prefix_tiles, sh.top_k)
+    P = sh.n_text + sh.n_audio
+    g = None if gate is None else bf16_to_f64(gate)
+    out = round_bf16(attention(q, k, v, ts, n_prefix_tiles, P, rt, bool(sh.pooled), rows, g))
+    return dict(out=out, **rt)
