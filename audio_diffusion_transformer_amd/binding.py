@@ -1,0 +1,198 @@
+"""ctypes binding of libh3.so: argument marshalling only.
+
+Every step of the forward runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers, numpy tile maps into host arrays and
+python shapes into the C structs declared in include/h3.h.  If the built
+library is missing, loading fails loudly: there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libh3.so")
+
+H3_OK, H3_EINVAL, H3_EWORKSPACE, H3_EHIP, H3_EUNSUPPORTED = 0, -1, -2, -3, -4
+H3_WS_BLOCK, H3_WS_DIT, H3_WS_ATTN = 0, 1, 2
+KERNEL_CLASSES = ["modnorm", "gemm_qkv", "heads", "route", "attn", "gemm_o", "gemm_fc1",
+                  "gemm_fc2", "final", "tables"]
+
+_vp = ctypes.c_void_p
+
+
+class H3Shape(ctypes.Structure):
+    _fields_ = [("n_text", ctypes.c_int32), ("n_audio", ctypes.c_int32),
+                ("n_video", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
+                ("n_prefix_tiles", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("pooled", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
+
+
+class H3BlockWeights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w_qkv", "b_qkv", "q_gain", "k_gain", "w_o", "b_o",
+                                   "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
+
+
+class H3HeadWeights(ctypes.Structure):
+    _fields_ = [("w_video", _vp), ("b_video", _vp), ("w_audio", _vp), ("b_audio", _vp),
+                ("c_video", ctypes.c_int32), ("c_audio", ctypes.c_int32)]
+
+
+class H3WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("tables", "norm", "big", "q", "k", "vt", "qbar",
+                                               "kbar", "vbar", "scores", "sel", "pooled",
+                                               "attn", "x1", "xa", "xb", "total")] + \
+               [("padded_rows", ctypes.c_int32), ("n_query_tiles", ctypes.c_int32),
+                ("n_sel", ctypes.c_int32)]
+
+
+class H3Error(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"h3 error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    L.h3_abi_version.restype = ctypes.c_int
+    L.h3_last_error.restype = ctypes.c_char_p
+    L.h3_workspace_bytes.argtypes = [ctypes.POINTER(H3Shape), i32p, ctypes.c_int32]
+    L.h3_workspace_bytes.restype = ctypes.c_size_t
+    L.h3_workspace_layout.argtypes = [ctypes.POINTER(H3Shape), i32p, ctypes.c_int32,
+                                      ctypes.POINTER(H3WsLayout)]
+    L.h3_block_forward.argtypes = [ctypes.POINTER(H3Shape), i32p, ctypes.POINTER(H3BlockWeights),
+                                   _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.h3_dit_forward.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32, i32p,
+                                 ctypes.POINTER(H3BlockWeights), ctypes.POINTER(H3HeadWeights),
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.h3_routed_attn.argtypes = [ctypes.POINTER(H3Shape), i32p, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, ctypes.c_size_t, _vp]
+    L.h3_prof_enable.argtypes = [ctypes.c_int]
+    L.h3_prof_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                               ctypes.POINTER(ctypes.c_double)]
+    L.h3_prof_kernel_name.argtypes = [ctypes.c_int32]
+    L.h3_prof_kernel_name.restype = ctypes.c_char_p
+    for f in (L.h3_workspace_layout, L.h3_block_forward, L.h3_dit_forward, L.h3_routed_attn,
+              L.h3_prof_enable, L.h3_prof_read):
+        f.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def last_error():
+    return lib().h3_last_error().decode()
+
+
+def _check(rc):
+    if rc != H3_OK:
+        raise H3Error(rc, last_error())
+
+
+def make_shape(sh, tile_start, n_prefix_tiles):
+    """sh: any object with the fields of synth.Shape."""
+    return H3Shape(sh.n_text, sh.n_audio, sh.n_video, sh.hidden, sh.n_heads, sh.head_dim,
+                   sh.ffn, len(tile_start) - 1, n_prefix_tiles, sh.top_k, int(sh.pooled),
+                   float(sh.norm_eps))
+
+
+def _tiles(tile_start):
+    ts = np.ascontiguousarray(tile_start, dtype=np.int32)
+    return ts, ts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_bytes(shape: H3Shape, tile_start, which):
+    ts, tp = _tiles(tile_start)
+    n = lib().h3_workspace_bytes(ctypes.byref(shape), tp, which)
+    if n == 0:
+        raise H3Error(H3_EINVAL, last_error())
+    return n
+
+
+def workspace_layout(shape: H3Shape, tile_start, which) -> H3WsLayout:
+    ts, tp = _tiles(tile_start)
+    out = H3WsLayout()
+    _check(lib().h3_workspace_layout(ctypes.byref(shape), tp, which, ctypes.byref(out)))
+    return out
+
+
+def block_weights_struct(w):
+    """w: dict of device torch tensors (bf16 or int16/uint16 raw bits)."""
+    return H3BlockWeights(*[_ptr(w[n]) for n, _ in H3BlockWeights._fields_])
+
+
+def head_weights_struct(hw):
+    return H3HeadWeights(_ptr(hw["w_video"]), _ptr(hw["b_video"]), _ptr(hw["w_audio"]),
+                         _ptr(hw["b_audio"]), int(hw["w_video"].shape[0]),
+                         int(hw["w_audio"].shape[0]))
+
+
+def block_forward(shape, tile_start, w, mod, rope, x_in, x_out, ws, stream=None):
+    ts, tp = _tiles(tile_start)
+    ws_struct = block_weights_struct(w) if isinstance(w, dict) else w
+    _check(lib().h3_block_forward(ctypes.byref(shape), tp, ctypes.byref(ws_struct), _ptr(mod),
+                                  _ptr(rope), _ptr(x_in), _ptr(x_out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dit_forward(shape, tile_start, blocks, heads, mod, mod_final, rope, x_in, vel_video,
+                vel_audio, ws, stream=None):
+    """blocks: list of weight dicts or a prebuilt (H3BlockWeights * L) array."""
+    ts, tp = _tiles(tile_start)
+    if isinstance(blocks, (list, tuple)):
+        arr = (H3BlockWeights * max(len(blocks), 1))(*[block_weights_struct(b) for b in blocks])
+        n = len(blocks)
+    else:
+        arr, n = blocks, len(blocks)
+    hw = head_weights_struct(heads) if isinstance(heads, dict) else heads
+    _check(lib().h3_dit_forward(ctypes.byref(shape), n, tp, arr, ctypes.byref(hw), _ptr(mod),
+                                _ptr(mod_final), _ptr(rope), _ptr(x_in), _ptr(vel_video),
+                                _ptr(vel_audio), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)))
+
+
+def routed_attn(shape, tile_start, q, k, v, out, ws, sel=None, scores=None, gate=None,
+                stream=None):
+    ts, tp = _tiles(tile_start)
+    _check(lib().h3_routed_attn(ctypes.byref(shape), tp, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                _ptr(out), _ptr(sel), _ptr(scores), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def prof_enable(on=True):
+    _check(lib().h3_prof_enable(1 if on else 0))
+
+
+def prof_read():
+    """{kernel class: (launches, total ms)} for the spans recorded since prof_enable."""
+    out = {}
+    for c, name in enumerate(KERNEL_CLASSES):
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(lib().h3_prof_read(c, ctypes.byref(n), ctypes.byref(ms)))
+        out[name] = (n.value, ms.value)
+    return out

@@ -1,0 +1,550 @@
+// C ABI of the library: argument validation, the workspace plan, and the
+// per-block launch sequence on the caller's stream.
+//
+// Block order (TensorFold PR #949, "What it adds": block.zig), each step one
+// kernel of this library:
+//   1 modnorm   x  -> n1                     (shift1, scale1)
+//   2 gemm      n1 . Wqkv^T + b -> y        (bias, bf16)
+//   3 heads     y  -> q~, k~ (norm, gain, rope), v^T, fp32 tile means
+//   4 route     tile scores, top-k, pooled branch
+//   5 attn      routed / dense attention -> attn [R][H]
+//   6 gemm      x1 = bf(x + gate1 * bf(attn . Wo^T + bo))
+//   7 modnorm   x1 -> n2                     (shift2, scale2)
+//   8 gemm      h  = bf(gelu(n2 . W1^T + b1))
+//   9 gemm      x2 = bf(x1 + gate2 * bf(h . W2^T + b2))
+// Activation arenas are reused as in the h3.c README's notes on activation
+// lifetimes: one [R][H] buffer holds n1 then n2, one [R][max(3H, F)] buffer
+// holds the QKV output then the MLP activations.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "internal.h"
+
+namespace h3 {
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  h3_shape s;
+  int R, P, H, D, F, nh, nT, npt, nQ, nsel, Rp, n_chunks, n_prefix_chunks, nqb, nqb_dense;
+  std::vector<int> tstart, tpstart, chunk_valid, qblocks;
+  h3_ws_layout lay;
+  size_t off_tstart, off_tpstart, off_chunk, off_qb;
+};
+
+int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) {
+  if (!s) return fail(H3_EINVAL, "shape is NULL");
+  if (!tile_start) return fail(H3_EINVAL, "tile_start is NULL");
+  if (which < H3_WS_BLOCK || which > H3_WS_ATTN) return fail(H3_EINVAL, "bad workspace kind %d", which);
+  p.s = *s;
+  if (s->n_text < 0 || s->n_audio < 0 || s->n_video < 0)
+    return fail(H3_EINVAL, "negative row count");
+  p.R = s->n_text + s->n_audio + s->n_video;
+  p.P = s->n_text + s->n_audio;
+  if (p.R < 1) return fail(H3_EINVAL, "no rows");
+  if (s->n_heads < 1 || s->head_dim < 1) return fail(H3_EINVAL, "bad heads");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(H3_EUNSUPPORTED, "head_dim %d not in {64, 128}", s->head_dim);
+  p.D = s->head_dim;
+  p.nh = s->n_heads;
+  p.H = s->hidden;
+  if (which != H3_WS_ATTN) {
+    if (p.H != p.nh * p.D) return fail(H3_EINVAL, "hidden %d != n_heads * head_dim", p.H);
+    if (p.H % 256 != 0 || p.H > 8192)
+      return fail(H3_EUNSUPPORTED, "hidden %d must be a multiple of 256 and <= 8192", p.H);
+    if (s->ffn < 256 || s->ffn % 256 != 0)
+      return fail(H3_EUNSUPPORTED, "ffn %d must be a positive multiple of 256", s->ffn);
+  } else {
+    p.H = p.nh * p.D;
+  }
+  p.F = s->ffn;
+  if (!(s->norm_eps >= 0.f)) return fail(H3_EINVAL, "norm_eps must be >= 0");
+  p.nT = s->n_tiles;
+  p.npt = s->n_prefix_tiles;
+  if (p.nT < 1 || p.npt < 0 || p.npt > p.nT) return fail(H3_EINVAL, "bad tile counts");
+  if (p.nT > 2048) return fail(H3_EUNSUPPORTED, "n_tiles %d > 2048", p.nT);
+  p.tstart.assign(tile_start, tile_start + p.nT + 1);
+  if (p.tstart[0] != 0 || p.tstart[p.nT] != p.R)
+    return fail(H3_EINVAL, "tile map must start at 0 and end at R=%d", p.R);
+  for (int t = 0; t < p.nT; ++t)
+    if (p.tstart[t + 1] <= p.tstart[t]) return fail(H3_EINVAL, "tile map not increasing at %d", t);
+  if (p.tstart[p.npt] != p.P)
+    return fail(H3_EINVAL, "prefix tiles end at row %d, prefix has %d rows", p.tstart[p.npt], p.P);
+  p.nQ = p.nT - p.npt;
+  if (p.nQ > 0 && s->top_k < 1) return fail(H3_EINVAL, "top_k must be >= 1");
+  p.nsel = p.nQ > 0 ? (s->top_k < p.nQ ? s->top_k : p.nQ) : 0;
+  if (!route_shape_ok(p.nT, p.nsel)) return fail(H3_EUNSUPPORTED, "top_k too large");
+
+  p.tpstart.resize(p.nT + 1);
+  p.tpstart[0] = 0;
+  for (int t = 0; t < p.nT; ++t) {
+    const int len = p.tstart[t + 1] - p.tstart[t];
+    p.tpstart[t + 1] = p.tpstart[t] + ((len + 31) / 32) * 32;
+  }
+  p.Rp = p.tpstart[p.nT];
+  p.n_chunks = p.Rp / 32;
+  p.n_prefix_chunks = p.tpstart[p.npt] / 32;
+  if (!attn_shape_ok(p.n_chunks, p.nsel)) return fail(H3_EUNSUPPORTED, "too many key chunks");
+  p.chunk_valid.assign(p.n_chunks, 0);
+  for (int t = 0; t < p.nT; ++t) {
+    const int len = p.tstart[t + 1] - p.tstart[t];
+    for (int o = 0; o < len; o += 32)
+      p.chunk_valid[(p.tpstart[t] + o) / 32] = len - o < 32 ? len - o : 32;
+  }
+  p.qblocks.clear();
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int t = pass == 0 ? 0 : p.npt; t < (pass == 0 ? p.npt : p.nT); ++t) {
+      const int len = p.tstart[t + 1] - p.tstart[t];
+      for (int o = 0; o < len; o += 64) {
+        p.qblocks.push_back(t);
+        p.qblocks.push_back(p.tpstart[t] + o);
+        p.qblocks.push_back(len - o < 64 ? len - o : 64);
+        p.qblocks.push_back(p.tstart[t] + o);
+      }
+    }
+    if (pass == 0) p.nqb_dense = (int)p.qblocks.size() / 4;
+  }
+  p.nqb = (int)p.qblocks.size() / 4;
+
+  // ---- workspace layout ----
+  h3_ws_layout& L = p.lay;
+  L = h3_ws_layout{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t bf = 2, f4 = 4;
+  L.tables = off;
+  p.off_tstart = take((size_t)(p.nT + 1) * 4);
+  p.off_tpstart = take((size_t)(p.nT + 1) * 4);
+  p.off_chunk = take((size_t)p.n_chunks * 4);
+  p.off_qb = take((size_t)p.nqb * 16);
+  const size_t R = p.R, H = p.H;
+  if (which != H3_WS_ATTN) {
+    L.norm = take(R * H * bf);
+    L.big = take(R * (size_t)(3 * p.H > p.F ? 3 * p.H : p.F) * bf);
+  }
+  L.q = take((size_t)p.nh * p.Rp * p.D * bf);
+  L.k = take((size_t)p.nh * p.Rp * p.D * bf);
+  L.vt = take((size_t)p.nh * p.Rp * p.D * bf);
+  L.qbar = take((size_t)p.nh * (p.nQ > 0 ? p.nQ : 1) * p.D * f4);
+  L.kbar = take((size_t)p.nh * p.nT * p.D * f4);
+  L.vbar = take((size_t)p.nh * p.nT * p.D * f4);
+  L.scores = take((size_t)p.nh * (p.nQ > 0 ? p.nQ : 1) * p.nT * f4);
+  L.sel = take((size_t)p.nh * (p.nQ > 0 ? p.nQ : 1) * (p.nsel > 0 ? p.nsel : 1) * 4);
+  L.pooled = take((size_t)p.nh * (p.nQ > 0 ? p.nQ : 1) * p.D * f4);
+  if (which != H3_WS_ATTN) {
+    L.attn = take(R * H * bf);
+    L.x1 = take(R * H * bf);
+  }
+  if (which == H3_WS_DIT) {
+    L.xa = take(R * H * bf);
+    L.xb = take(R * H * bf);
+  }
+  L.total = off;
+  L.padded_rows = p.Rp;
+  L.n_query_tiles = p.nQ;
+  L.n_sel = p.nsel;
+  return H3_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(H3_EINVAL, "workspace is NULL");
+  if (((uintptr_t)ws & 255) != 0) return fail(H3_EINVAL, "workspace must be 256-byte aligned");
+  if (ws_bytes < p.lay.total)
+    return fail(H3_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.lay.total);
+  return H3_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+#define H3_TRY(expr)                                                        \
+  do {                                                                      \
+    hipError_t e_ = (expr);                                                 \
+    if (e_ != hipSuccess) return fail(H3_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+int upload_tables(const Plan& p, void* ws, hipStream_t st) {
+  prof_begin(H3_K_TABLES, st);
+  H3_TRY(launch_poke(at<int>(ws, p.off_tstart), p.tstart.data(), (int)p.tstart.size(), st));
+  H3_TRY(launch_poke(at<int>(ws, p.off_tpstart), p.tpstart.data(), (int)p.tpstart.size(), st));
+  H3_TRY(launch_poke(at<int>(ws, p.off_chunk), p.chunk_valid.data(), (int)p.chunk_valid.size(), st));
+  H3_TRY(launch_poke(at<int>(ws, p.off_qb), p.qblocks.data(), (int)p.qblocks.size(), st));
+  prof_end(H3_K_TABLES, st);
+  return H3_OK;
+}
+
+HeadsArgs heads_args(const Plan& p, void* ws) {
+  HeadsArgs a{};
+  a.q = at<bf16_t>(ws, p.lay.q);
+  a.k = at<bf16_t>(ws, p.lay.k);
+  a.vt = at<bf16_t>(ws, p.lay.vt);
+  a.qbar = at<float>(ws, p.lay.qbar);
+  a.kbar = at<float>(ws, p.lay.kbar);
+  a.vbar = at<float>(ws, p.lay.vbar);
+  a.tstart = at<int>(ws, p.off_tstart);
+  a.tpstart = at<int>(ws, p.off_tpstart);
+  a.R = p.R;
+  a.Rp = p.Rp;
+  a.nh = p.nh;
+  a.nT = p.nT;
+  a.npt = p.npt;
+  a.H = p.H;
+  a.eps = p.s.norm_eps;
+  return a;
+}
+
+int run_attention(const Plan& p, void* ws, int32_t* sel_out, float* scores_out, bf16_t* out,
+                  hipStream_t st) {
+  int* sel = sel_out ? sel_out : at<int>(ws, p.lay.sel);
+  float* scores = scores_out ? scores_out : at<float>(ws, p.lay.scores);
+  if (p.nQ > 0) {
+    RouteArgs r{};
+    r.qbar = at<float>(ws, p.lay.qbar);
+    r.kbar = at<float>(ws, p.lay.kbar);
+    r.vbar = at<float>(ws, p.lay.vbar);
+    r.scores = scores;
+    r.sel = sel;
+    r.pooled = at<float>(ws, p.lay.pooled);
+    r.nh = p.nh;
+    r.nQ = p.nQ;
+    r.nT = p.nT;
+    r.npt = p.npt;
+    r.top_k = p.s.top_k;
+    r.nsel = p.nsel;
+    r.use_pooled = p.s.pooled ? 1 : 0;
+    prof_begin(H3_K_ROUTE, st);
+    H3_TRY(launch_route(p.D, r, st));
+    prof_end(H3_K_ROUTE, st);
+  }
+  AttnArgs a{};
+  a.q = at<bf16_t>(ws, p.lay.q);
+  a.k = at<bf16_t>(ws, p.lay.k);
+  a.vt = at<bf16_t>(ws, p.lay.vt);
+  a.sel = sel;
+  a.pooled = p.s.pooled ? at<float>(ws, p.lay.pooled) : nullptr;
+  a.tpstart = at<int>(ws, p.off_tpstart);
+  a.chunk_valid = at<int>(ws, p.off_chunk);
+  a.qblocks = at<int4>(ws, p.off_qb);
+  a.out = out;
+  a.nh = p.nh;
+  a.Rp = p.Rp;
+  a.H = p.nh * p.D;
+  a.nT = p.nT;
+  a.npt = p.npt;
+  a.nQ = p.nQ;
+  a.nsel = p.nsel;
+  a.nqb = p.nqb;
+  a.nqb_dense = p.nqb_dense;
+  a.n_prefix_chunks = p.n_prefix_chunks;
+  a.n_chunks = p.n_chunks;
+  prof_begin(H3_K_ATTN, st);
+  H3_TRY(launch_attn(p.D, a, st));
+  prof_end(H3_K_ATTN, st);
+  return H3_OK;
+}
+
+int check_block_weights(const h3_block_weights* w, int l) {
+  if (!w) return fail(H3_EINVAL, "block %d weights NULL", l);
+  const void* ptrs[] = {w->w_qkv, w->b_qkv, w->q_gain, w->k_gain, w->w_o,
+                        w->b_o,   w->w_fc1, w->b_fc1,  w->w_fc2,  w->b_fc2};
+  for (const void* q : ptrs) {
+    if (!q) return fail(H3_EINVAL, "block %d: a weight pointer is NULL", l);
+    if (!aligned16(q)) return fail(H3_EINVAL, "block %d: a weight pointer is not 16-byte aligned", l);
+  }
+  return H3_OK;
+}
+
+// Steps 1-9 of one block; tables already uploaded.
+int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* mod,
+              const float* rope, const bf16_t* x_in, bf16_t* x_out, hipStream_t st) {
+  const int R = p.R, H = p.H, F = p.F;
+  const int nt = p.s.n_text, np_ = p.P;
+  bf16_t* norm = at<bf16_t>(ws, p.lay.norm);
+  bf16_t* big = at<bf16_t>(ws, p.lay.big);
+  bf16_t* attn = at<bf16_t>(ws, p.lay.attn);
+  bf16_t* x1 = at<bf16_t>(ws, p.lay.x1);
+  const int ms = 6 * H;  // floats between segments of mod
+
+  prof_begin(H3_K_NORM, st);
+  H3_TRY(launch_modnorm(x_in, norm, 0, mod + 0 * H, mod + 1 * H, ms, 0, R, H, nt, np_,
+                        p.s.norm_eps, st));
+  prof_end(H3_K_NORM, st);
+
+  GemmEpi e{};
+  e.bias = w->b_qkv;
+  e.out = big;
+  e.n_text = nt;
+  e.n_prefix = np_;
+  prof_begin(H3_K_GEMM_QKV, st);
+  H3_TRY(launch_gemm(EPI_BIAS, norm, w->w_qkv, R, 3 * H, H, e, st));
+  prof_end(H3_K_GEMM_QKV, st);
+
+  HeadsArgs ha = heads_args(p, ws);
+  ha.y = big;
+  ha.q_gain = w->q_gain;
+  ha.k_gain = w->k_gain;
+  ha.rope = rope;
+  prof_begin(H3_K_HEADS, st);
+  H3_TRY(launch_heads(HEADS_QKV, p.D, ha, st));
+  prof_end(H3_K_HEADS, st);
+
+  int rc = run_attention(p, ws, nullptr, nullptr, attn, st);
+  if (rc) return rc;
+
+  e = GemmEpi{};
+  e.bias = w->b_o;
+  e.out = x1;
+  e.res = x_in;
+  e.gate = mod + 2 * H;
+  e.gate_seg_stride = ms;
+  e.n_text = nt;
+  e.n_prefix = np_;
+  prof_begin(H3_K_GEMM_O, st);
+  H3_TRY(launch_gemm(EPI_BIAS_RESGATE, attn, w->w_o, R, H, H, e, st));
+  prof_end(H3_K_GEMM_O, st);
+
+  prof_begin(H3_K_NORM, st);
+  H3_TRY(launch_modnorm(x1, norm, 0, mod + 3 * H, mod + 4 * H, ms, 0, R, H, nt, np_,
+                        p.s.norm_eps, st));
+  prof_end(H3_K_NORM, st);
+
+  e = GemmEpi{};
+  e.bias = w->b_fc1;
+  e.out = big;
+  prof_begin(H3_K_GEMM_FC1, st);
+  H3_TRY(launch_gemm(EPI_BIAS_GELU, norm, w->w_fc1, R, F, H, e, st));
+  prof_end(H3_K_GEMM_FC1, st);
+
+  e = GemmEpi{};
+  e.bias = w->b_fc2;
+  e.out = x_out;
+  e.res = x1;
+  e.gate = mod + 5 * H;
+  e.gate_seg_stride = ms;
+  e.n_text = nt;
+  e.n_prefix = np_;
+  prof_begin(H3_K_GEMM_FC2, st);
+  H3_TRY(launch_gemm(EPI_BIAS_RESGATE, big, w->w_fc2, R, H, F, e, st));
+  prof_end(H3_K_GEMM_FC2, st);
+  return H3_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel-time accounting
+// ---------------------------------------------------------------------------
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> spans;
+  std::vector<hipEvent_t> open;
+  int open_cls = -1;
+  int64_t launches[H3_K_COUNT] = {};
+  double ms[H3_K_COUNT] = {};
+} g_prof;
+
+hipEvent_t prof_event() {
+  if (g_prof.used == g_prof.pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_prof.pool.push_back(e);
+  }
+  return g_prof.pool[g_prof.used++];
+}
+
+hipEvent_t g_begin_ev = nullptr;
+
+}  // namespace
+
+void prof_begin(int cls, hipStream_t s) {
+  if (!g_prof.on) return;
+  g_begin_ev = prof_event();
+  g_prof.open_cls = cls;
+  if (g_begin_ev) (void)hipEventRecord(g_begin_ev, s);
+}
+
+void prof_end(int cls, hipStream_t s) {
+  if (!g_prof.on || !g_begin_ev) return;
+  hipEvent_t e = prof_event();
+  if (!e) return;
+  (void)hipEventRecord(e, s);
+  g_prof.spans.push_back({cls, {g_begin_ev, e}});
+  g_begin_ev = nullptr;
+}
+
+}  // namespace h3
+
+using namespace h3;
+
+extern "C" {
+
+int h3_abi_version(void) { return H3_ABI_VERSION; }
+
+const char* h3_last_error(void) { return g_err.c_str(); }
+
+size_t h3_workspace_bytes(const h3_shape* shape, const int32_t* tile_start, int32_t which) {
+  Plan p;
+  if (make_plan(shape, tile_start, which, p) != H3_OK) return 0;
+  return p.lay.total;
+}
+
+int h3_workspace_layout(const h3_shape* shape, const int32_t* tile_start, int32_t which,
+                        h3_ws_layout* out) {
+  if (!out) return fail(H3_EINVAL, "out is NULL");
+  Plan p;
+  int rc = make_plan(shape, tile_start, which, p);
+  if (rc) return rc;
+  *out = p.lay;
+  return H3_OK;
+}
+
+int h3_block_forward(const h3_shape* shape, const int32_t* tile_start, const h3_block_weights* w,
+                     const float* mod, const float* rope, const h3_bf16* x_in, h3_bf16* x_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, tile_start, H3_WS_BLOCK, p);
+  if (rc) return rc;
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if ((rc = check_block_weights(w, 0))) return rc;
+  if (!mod || !x_in || !x_out) return fail(H3_EINVAL, "mod, x_in and x_out are required");
+  if (!aligned16(mod) || !aligned16(x_in) || !aligned16(x_out) || (rope && !aligned16(rope)))
+    return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (x_in == x_out) return fail(H3_EINVAL, "x_out must not alias x_in");
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = upload_tables(p, ws, st))) return rc;
+  return run_block(p, ws, w, mod, rope, x_in, x_out, st);
+}
+
+int h3_dit_forward(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_start,
+                   const h3_block_weights* blocks, const h3_head_weights* heads,
+                   const float* mod, const float* mod_final, const float* rope,
+                   const h3_bf16* x_in, float* vel_video, float* vel_audio, void* ws,
+                   size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, tile_start, H3_WS_DIT, p);
+  if (rc) return rc;
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if (n_blocks < 0) return fail(H3_EINVAL, "n_blocks < 0");
+  if (n_blocks > 0 && !blocks) return fail(H3_EINVAL, "blocks is NULL");
+  for (int l = 0; l < n_blocks; ++l)
+    if ((rc = check_block_weights(&blocks[l], l))) return rc;
+  if (!heads || !heads->w_video || !heads->b_video || !heads->w_audio || !heads->b_audio)
+    return fail(H3_EINVAL, "head weights are required");
+  if (heads->c_video < 1 || heads->c_video > 256 || heads->c_audio < 1 || heads->c_audio > 256)
+    return fail(H3_EINVAL, "head widths must be in [1, 256]");
+  if ((n_blocks > 0 && !mod) || !mod_final || !x_in)
+    return fail(H3_EINVAL, "mod, mod_final and x_in are required");
+  if ((p.s.n_video > 0 && !vel_video) || (p.s.n_audio > 0 && !vel_audio))
+    return fail(H3_EINVAL, "velocity outputs are required");
+  if (!aligned16(x_in) || (mod && !aligned16(mod)) || !aligned16(mod_final) ||
+      (rope && !aligned16(rope)) || !aligned16(heads->w_video) || !aligned16(heads->w_audio))
+    return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = upload_tables(p, ws, st))) return rc;
+  const bf16_t* x = x_in;
+  bf16_t* xa = at<bf16_t>(ws, p.lay.xa);
+  bf16_t* xb = at<bf16_t>(ws, p.lay.xb);
+  const size_t mstride = (size_t)3 * 6 * p.H;
+  for (int l = 0; l < n_blocks; ++l) {
+    bf16_t* xo = (l & 1) ? xb : xa;
+    if ((rc = run_block(p, ws, &blocks[l], mod + l * mstride, rope, x, xo, st))) return rc;
+    x = xo;
+  }
+  // final modulated norm of the audio and video rows, then the heads
+  bf16_t* z = at<bf16_t>(ws, p.lay.norm);
+  const int H = p.H, nt = p.s.n_text;
+  prof_begin(H3_K_FINAL, st);
+  H3_TRY(launch_modnorm(x, z, nt, mod_final + 0 * H, mod_final + 1 * H, 2 * H, nt, p.R, H, nt,
+                        p.P, p.s.norm_eps, st));
+  H3_TRY(launch_out_head(z, p.s.n_audio, H, heads->w_audio, heads->b_audio, heads->c_audio,
+                         vel_audio, st));
+  H3_TRY(launch_out_head(z + (size_t)p.s.n_audio * H, p.s.n_video, H, heads->w_video,
+                         heads->b_video, heads->c_video, vel_video, st));
+  prof_end(H3_K_FINAL, st);
+  return H3_OK;
+}
+
+int h3_routed_attn(const h3_shape* shape, const int32_t* tile_start, const h3_bf16* q,
+                   const h3_bf16* k, const h3_bf16* v, const h3_bf16* gate, h3_bf16* out,
+                   int32_t* sel, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, tile_start, H3_WS_ATTN, p);
+  if (rc) return rc;
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if (gate) return fail(H3_EUNSUPPORTED, "a gated pooled branch is not supported");
+  if (!q || !k || !v || !out) return fail(H3_EINVAL, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = upload_tables(p, ws, st))) return rc;
+  HeadsArgs ha = heads_args(p, ws);
+  ha.q_in = q;
+  ha.k_in = k;
+  ha.v_in = v;
+  prof_begin(H3_K_HEADS, st);
+  H3_TRY(launch_heads(HEADS_SPLIT, p.D, ha, st));
+  prof_end(H3_K_HEADS, st);
+  return run_attention(p, ws, sel, scores, out, st);
+}
+
+int h3_prof_enable(int on) {
+  g_prof.on = on != 0;
+  g_prof.spans.clear();
+  g_prof.used = 0;
+  for (int c = 0; c < H3_K_COUNT; ++c) {
+    g_prof.launches[c] = 0;
+    g_prof.ms[c] = 0.0;
+  }
+  return H3_OK;
+}
+
+int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms) {
+  if (cls < 0 || cls >= H3_K_COUNT) return fail(H3_EINVAL, "bad kernel class");
+  for (auto& sp : g_prof.spans) {
+    float ms = 0.f;
+    if (hipEventSynchronize(sp.second.second) != hipSuccess) return fail(H3_EHIP, "event sync");
+    if (hipEventElapsedTime(&ms, sp.second.first, sp.second.second) != hipSuccess)
+      return fail(H3_EHIP, "event elapsed");
+    g_prof.launches[sp.first] += 1;
+    g_prof.ms[sp.first] += ms;
+  }
+  g_prof.spans.clear();
+  g_prof.used = 0;
+  if (launches) *launches = g_prof.launches[cls];
+  if (total_ms) *total_ms = g_prof.ms[cls];
+  return H3_OK;
+}
+
+const char* h3_prof_kernel_name(int32_t cls) {
+  static const char* names[H3_K_COUNT] = {"modnorm", "gemm_qkv", "heads", "route", "attn",
+                                          "gemm_o", "gemm_fc1", "gemm_fc2", "final", "tables"};
+  return (cls >= 0 && cls < H3_K_COUNT) ? names[cls] : "";
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Host-side declarations shared by the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "h3.h"
+
+namespace h3 {
+
+typedef uint16_t bf16_t;
+
+// Per-kernel-class event bracketing (enabled by h3_prof_enable).
+void prof_begin(int cls, hipStream_t s);
+void prof_end(int cls, hipStream_t s);
+
+// ---- modulated RMS norm ----------------------------------------------------
+// out[r] = bf(x[r] * (mean(x[r]^2) + eps)^-1/2 * (1 + scale[seg]) + shift[seg])
+// for rows r in [row0, row1); shift/scale of segment s at base + s*seg_stride.
+// out row index is (r - out_row0).
+hipError_t launch_modnorm(const bf16_t* x, bf16_t* out, int out_row0, const float* shift,
+                          const float* scale, int seg_stride, int row0, int row1, int H,
+                          int n_text, int n_prefix, float eps, hipStream_t s);
+
+// ---- GEMM: C[M][N] = A[M][K] * B[N][K]^T with a fused epilogue -------------
+enum { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESGATE = 2 };
+struct GemmEpi {
+  const bf16_t* bias;   // [N]
+  bf16_t* out;          // [M][N]
+  const bf16_t* res;    // [M][N] residual input (EPI_BIAS_RESGATE)
+  const float* gate;    // gate of segment s, column n at gate[s * gate_seg_stride + n]
+  int gate_seg_stride;
+  int n_text, n_prefix; // row segment boundaries
+};
+bool gemm_shape_ok(int M, int N, int K);
+hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, int K,
+                       const GemmEpi& ep, hipStream_t s);
+
+// ---- head layout: q/k RMS norm + RoPE, padded head-major q, k, v^T, tile means
+struct HeadsArgs {
+  // source: MODE_QKV: y [R][3H] (per-head [q|k|v] interleaved);
+  //         MODE_SPLIT: q, k, v [nh][R][d]
+  const bf16_t* y;
+  const bf16_t* q_in;
+  const bf16_t* k_in;
+  const bf16_t* v_in;
+  const bf16_t* q_gain;  // [d] (MODE_QKV)
+  const bf16_t* k_gain;
+  const float* rope;     // [R][d/2][2] or null (MODE_QKV)
+  bf16_t* q;             // [nh][Rp][d]
+  bf16_t* k;             // [nh][Rp][d]
+  bf16_t* vt;            // [nh][d][Rp]
+  float* qbar;           // [nh][nQ][d]
+  float* kbar;           // [nh][nT][d]
+  float* vbar;           // [nh][nT][d]
+  const int* tstart;     // [nT+1] real rows
+  const int* tpstart;    // [nT+1] padded rows
+  int R, Rp, nh, nT, npt, H;
+  float eps;
+};
+enum { HEADS_QKV = 0, HEADS_SPLIT = 1 };
+hipError_t launch_heads(int mode, int head_dim, const HeadsArgs& a, hipStream_t s);
+
+// ---- routing: tile scores, top-k, pooled branch ------------------------------
+struct RouteArgs {
+  const float* qbar;    // [nh][nQ][d]
+  const float* kbar;    // [nh][nT][d]
+  const float* vbar;    // [nh][nT][d]
+  float* scores;        // [nh][nQ][nT]
+  int* sel;             // [nh][nQ][nsel]
+  float* pooled;        // [nh][nQ][d]
+  int nh, nQ, nT, npt, top_k, nsel, use_pooled;
+};
+bool route_shape_ok(int nT, int top_k);
+hipError_t launch_route(int head_dim, const RouteArgs& a, hipStream_t s);
+
+// ---- attention ---------------------------------------------------------------
+struct AttnArgs {
+  const bf16_t* q;          // [nh][Rp][d]
+  const bf16_t* k;          // [nh][Rp][d]
+  const bf16_t* vt;         // [nh][d][Rp]
+  const int* sel;           // [nh][nQ][nsel]
+  const float* pooled;      // [nh][nQ][d] or null
+  const int* tpstart;       // [nT+1]
+  const int* chunk_valid;   // [Rp/32]
+  const int4* qblocks;      // [nqb]: (tile, padded row0, nrows, real row0)
+  bf16_t* out;              // [R][H]
+  int nh, Rp, H, nT, npt, nQ, nsel, nqb, nqb_dense, n_prefix_chunks, n_chunks;
+};
+bool attn_shape_ok(int n_chunks, int nsel);
+hipError_t launch_attn(int head_dim, const AttnArgs& a, hipStream_t s);
+
+// ---- output heads: vel[r][c] = z[r] . W[c] + b[c] (fp32 out) --------------------
+hipError_t launch_out_head(const bf16_t* z, int rows, int H, const bf16_t* w, const bf16_t* b,
+                           int C, float* vel, hipStream_t s);
+
+// ---- small table upload through kernel arguments ------------------------------
+hipError_t launch_poke(int* dst, const int* src, int n, hipStream_t s);
+
+}  // namespace h3

@@ -1,0 +1,180 @@
+/*
+ * h3.h -- C ABI of the MI355X (gfx950) forward of an H3-style joint
+ * video+audio diffusion transformer.
+ *
+ * The computation follows "TensorFold PR #949" (FastH3 DiT forward on Zig +
+ * Metal): sections "Precision is the checkpoint's own" (bf16 weights and
+ * activations, fp32 sums, fp32 tile means / scores / top-k / pooled branch,
+ * softmax weights rounded to bf16 before the value product) and "What it
+ * adds" (one block: modulated norm, q/k/v products, head layout with q/k
+ * norm and rotary, tile means, tile scores, top-k, pooled branch,
+ * tile-routed attention with an online softmax, out projection, MLP), and
+ * the h3.c README ("Antirez/h3.c: MiniMax H3 inference engine for Mac
+ * computers": fused gated AdaLN with rounded bf16 residuals, QKV rows
+ * interleaved per attention head, bf16 output heads, F32 rows out).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  bf16 values
+ *     are raw 16-bit patterns (h3_bf16).  Layouts are dense row-major as
+ *     written next to each argument; weights follow the [out][in] convention.
+ *   - Host structs (h3_shape, weights tables) and tile_start are HOST memory,
+ *     read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous: shapes are validated on the host
+ *     before any launch; device faults surface at the caller's next sync.
+ *   - The library allocates no device memory and keeps no pointer after it
+ *     returns.  Scratch lives in the caller's workspace `ws` (256-byte
+ *     aligned, at least h3_workspace_bytes() bytes).  Concurrent calls need
+ *     distinct workspaces.
+ *   - Outputs must not alias inputs.  Pointers must be 16-byte aligned.
+ *   - Same inputs on the same device give byte-identical outputs (no float
+ *     atomics; every reduction has a fixed order).
+ *   - Return value: H3_OK, or a negative code with a message available from
+ *     h3_last_error() (thread-local).
+ *
+ * Packed rows: R = n_text + n_audio + n_video rows, in that order; the first
+ * P = n_text + n_audio rows are the prefix.  The tile map tile_start[0..n_tiles]
+ * is strictly increasing, tile_start[0] = 0, tile_start[n_tiles] = R, and
+ * segment boundaries fall on tile boundaries: tiles [0, n_prefix_tiles) cover
+ * the prefix rows, the rest cover the video rows (the "video tiles").
+ */
+#ifndef H3_H
+#define H3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t h3_bf16;
+
+enum {
+  H3_OK = 0,
+  H3_EINVAL = -1,       /* bad shape, tile map or null required pointer */
+  H3_EWORKSPACE = -2,   /* ws_bytes smaller than h3_workspace_bytes() */
+  H3_EHIP = -3,         /* a HIP launch or runtime error */
+  H3_EUNSUPPORTED = -4  /* valid but not supported (e.g. head_dim not 64/128) */
+};
+
+enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2 };
+
+#define H3_ABI_VERSION 1
+
+typedef struct {
+  int32_t n_text, n_audio, n_video;  /* packed in this order */
+  int32_t hidden;                    /* H = n_heads * head_dim; multiple of 256, <= 8192 */
+  int32_t n_heads, head_dim;         /* head_dim in {64, 128} */
+  int32_t ffn;                       /* F, multiple of 256 */
+  int32_t n_tiles, n_prefix_tiles;   /* tile map size; prefix tiles cover rows [0, P) */
+  int32_t top_k;                     /* video key tiles per (head, video query tile); >= nQ keeps all */
+  int32_t pooled;                    /* 1: add the pooled branch to video rows */
+  float norm_eps;                    /* eps of the RMS norms (activation and Q/K) */
+} h3_shape;
+
+/* One block's weights, all bf16, device pointers. */
+typedef struct {
+  const h3_bf16 *w_qkv, *b_qkv;  /* [3H][H], [3H]; output rows per head interleaved [h][q|k|v][d] */
+  const h3_bf16 *q_gain, *k_gain;/* [d] each: gains of the per-head Q/K RMS norm */
+  const h3_bf16 *w_o, *b_o;      /* [H][H], [H] */
+  const h3_bf16 *w_fc1, *b_fc1;  /* [F][H], [F] */
+  const h3_bf16 *w_fc2, *b_fc2;  /* [H][F], [H] */
+} h3_block_weights;
+
+/* Output heads of the forward (bf16, device). */
+typedef struct {
+  const h3_bf16 *w_video, *b_video;  /* [c_video][H], [c_video] */
+  const h3_bf16 *w_audio, *b_audio;  /* [c_audio][H], [c_audio] */
+  int32_t c_video, c_audio;          /* each in [1, 256] */
+} h3_head_weights;
+
+/* Byte offsets of the intermediates inside a block workspace (for tests and
+ * diagnostics).  After h3_block_forward returns (and the stream is synced)
+ * the workspace holds: n2 (the MLP norm output, [R][H] bf16, in `norm`),
+ * the GELU activations ([R][F] bf16, in `big`), the head-major padded
+ * q, k ([nh][Rp][d] bf16) and v transposed ([nh][d][Rp] bf16), the tile
+ * means (fp32 [nh][nQ][d], [nh][n_tiles][d] x2), scores (fp32
+ * [nh][nQ][n_tiles]), sel (int32 [nh][nQ][min(top_k, nQ)]), pooled (fp32
+ * [nh][nQ][d]), attn ([R][H] bf16) and x1 ([R][H] bf16).  Padded row space:
+ * tile t occupies rows [tile_pstart[t], tile_pstart[t+1]) with
+ * tile_pstart[t+1] - tile_pstart[t] = 32 * ceil(len_t / 32); its first len_t
+ * rows are the tile's rows in order, the rest are zero. */
+typedef struct {
+  size_t tables, norm, big, q, k, vt, qbar, kbar, vbar, scores, sel, pooled, attn, x1;
+  size_t xa, xb;         /* residual ping-pong of h3_dit_forward (0 if unused) */
+  size_t total;
+  int32_t padded_rows;   /* Rp */
+  int32_t n_query_tiles; /* nQ = n_tiles - n_prefix_tiles */
+  int32_t n_sel;         /* min(top_k, nQ) */
+} h3_ws_layout;
+
+int h3_abi_version(void);
+const char* h3_last_error(void);
+
+/* Bytes of workspace needed by the entry point `which` (H3_WS_*) for this
+ * shape and tile map; 0 on invalid input (see h3_last_error). */
+size_t h3_workspace_bytes(const h3_shape* shape, const int32_t* tile_start, int32_t which);
+
+/* Offsets of the workspace regions (see h3_ws_layout).  Returns H3_OK or an error. */
+int h3_workspace_layout(const h3_shape* shape, const int32_t* tile_start, int32_t which,
+                        h3_ws_layout* out);
+
+/* One DiT block (TensorFold PR #949, "What it adds": block.zig; GELU MLP):
+ *   n1 = bf(x rms(x)^-1 (1 + scale1[seg]) + shift1[seg])
+ *   y  = bf(n1 Wqkv^T + b);  per head q, k, v;  q~, k~ = bf(rope(rmsnorm(.) gain))
+ *   routing on q~, k~, v: fp32 tile means and scores, top-k video key tiles
+ *   (NaN ranks -inf, ties to the lower tile), pooled branch
+ *   attn = bf(attention): text/audio rows dense over all rows; video rows over
+ *          the prefix rows plus the selected tiles, + pooled if enabled
+ *   x1 = bf(x + gate1[seg] bf(attn Wo^T + bo))
+ *   n2 = bf(x1 rms(x1)^-1 (1 + scale2[seg]) + shift2[seg])
+ *   x2 = bf(x1 + gate2[seg] bf(bf(gelu(n2 W1^T + b1)) W2^T + b2))
+ * mod:  fp32 [3 segments][6][H], vectors (shift1, scale1, gate1, shift2, scale2, gate2).
+ * rope: fp32 [R][d/2][2] (cos, sin) for the pairs (i, i + d/2), or NULL (no rotation).
+ * x_in, x_out: [R][H] bf16.  Workspace: H3_WS_BLOCK. */
+int h3_block_forward(const h3_shape* shape, const int32_t* tile_start,
+                     const h3_block_weights* w, const float* mod, const float* rope,
+                     const h3_bf16* x_in, h3_bf16* x_out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* The forward: n_blocks blocks (blocks: HOST array of n_blocks weight tables;
+ * mod: fp32 [n_blocks][3][6][H]), then the final modulated norm of the audio
+ * and video rows (mod_final: fp32 [3 segments][2][H], (shift, scale)) and the
+ * output heads, F32 with no rounding:
+ *   vel_video [n_video][c_video], vel_audio [n_audio][c_audio]  (fp32, device).
+ * h3.c README (final audio/video AdaLN, bf16 heads); TensorFold PR #949 (raw
+ * f32 rows out).  Workspace: H3_WS_DIT. */
+int h3_dit_forward(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_start,
+                   const h3_block_weights* blocks, const h3_head_weights* heads,
+                   const float* mod, const float* mod_final, const float* rope,
+                   const h3_bf16* x_in, float* vel_video, float* vel_audio,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Routed attention alone on head-major q, k, v ([nh][R][d] bf16): tile
+ * means, scores, top-k, pooled branch and attention as in h3_block_forward.
+ *   out:    [R][nh*d] bf16.
+ *   gate:   must be NULL (a gated pooled branch is not supported yet).
+ *   sel:    NULL or int32 [nh][nQ][min(top_k, nQ)]: selected tile ids, ascending.
+ *   scores: NULL or fp32 [nh][nQ][n_tiles]: the tile scores.
+ * Workspace: H3_WS_ATTN. */
+int h3_routed_attn(const h3_shape* shape, const int32_t* tile_start,
+                   const h3_bf16* q, const h3_bf16* k, const h3_bf16* v,
+                   const h3_bf16* gate, h3_bf16* out, int32_t* sel, float* scores,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel-time accounting for diagnostics: while enabled, each kernel launch
+ * of the library is bracketed by HIP events on its stream.  h3_prof_read
+ * synchronizes those events and returns, for kernel class `cls` (H3_K_*),
+ * the launch count and the summed duration in milliseconds; it then forgets
+ * the events it has read.  Not thread-safe; for benchmarks. */
+enum { H3_K_NORM = 0, H3_K_GEMM_QKV, H3_K_HEADS, H3_K_ROUTE, H3_K_ATTN, H3_K_GEMM_O,
+       H3_K_GEMM_FC1, H3_K_GEMM_FC2, H3_K_FINAL, H3_K_TABLES, H3_K_COUNT };
+int h3_prof_enable(int on);
+int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms);
+const char* h3_prof_kernel_name(int32_t cls);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H3_H */

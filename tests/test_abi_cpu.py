@@ -1,0 +1,110 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects invalid shapes on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from audio_diffusion_transformer_amd import binding as B
+from audio_diffusion_transformer_amd import synth as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "h3.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from audio_diffusion_transformer_amd import build
+        build.build_hip()
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.h3_abi_version() == 1
+
+
+def _shape(sh):
+    ts, npt = S.tile_map(sh)
+    return B.make_shape(sh, ts, npt), ts
+
+
+def test_workspace_layout_is_consistent(lib):
+    for sh in (S.TINY, S.MID, S.FULL):
+        shape, ts = _shape(sh)
+        for which in (B.H3_WS_BLOCK, B.H3_WS_DIT, B.H3_WS_ATTN):
+            n = B.workspace_bytes(shape, ts, which)
+            lay = B.workspace_layout(shape, ts, which)
+            assert lay.total == n
+            lens = np.diff(ts)
+            assert lay.padded_rows == int(np.sum((lens + 31) // 32 * 32))
+            assert lay.n_query_tiles == len(ts) - 1 - shape.n_prefix_tiles
+            assert lay.n_sel == min(sh.top_k, lay.n_query_tiles)
+            offs = [lay.q, lay.k, lay.vt, lay.qbar, lay.kbar, lay.vbar, lay.scores, lay.sel,
+                    lay.pooled]
+            assert all(o % 256 == 0 for o in offs)
+            assert offs == sorted(offs) and offs[-1] < n
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda s, t: setattr(s, "head_dim", 96), B.H3_EUNSUPPORTED),
+    (lambda s, t: setattr(s, "hidden", 300), B.H3_EINVAL),
+    (lambda s, t: setattr(s, "ffn", 1000), B.H3_EUNSUPPORTED),
+    (lambda s, t: setattr(s, "n_prefix_tiles", 1), B.H3_EINVAL),
+    (lambda s, t: t.__setitem__(3, t[2]), B.H3_EINVAL),
+    (lambda s, t: t.__setitem__(-1, t[-1] + 1), B.H3_EINVAL),
+    (lambda s, t: setattr(s, "top_k", 0), B.H3_EINVAL),
+    (lambda s, t: setattr(s, "n_text", -1), B.H3_EINVAL),
+])
+def test_invalid_shapes_rejected_on_host(lib, mutate, code):
+    shape, ts = _shape(S.TINY)
+    ts = ts.copy()
+    mutate(shape, ts)
+    lay = B.H3WsLayout()
+    rc = lib.h3_workspace_layout(ctypes.byref(shape),
+                                 ts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 B.H3_WS_BLOCK, ctypes.byref(lay))
+    assert rc == code, B.last_error()
+    assert B.last_error()
+    assert lib.h3_workspace_bytes(ctypes.byref(shape),
+                                  ts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                  B.H3_WS_BLOCK) == 0
+
+
+def test_entry_points_validate_before_launch(lib):
+    """Null or undersized arguments are refused with an error code; nothing is
+    launched (this runs without a GPU)."""
+    shape, ts = _shape(S.TINY)
+    tp = ts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    w = B.H3BlockWeights()
+    rc = lib.h3_block_forward(ctypes.byref(shape), tp, ctypes.byref(w), None, None, None, None,
+                              None, 0, None)
+    assert rc == B.H3_EINVAL and "workspace" in B.last_error()
+    rc = lib.h3_block_forward(ctypes.byref(shape), tp, ctypes.byref(w), None, None, None, None,
+                              ctypes.c_void_p(256), 16, None)
+    assert rc == B.H3_EWORKSPACE
+    rc = lib.h3_routed_attn(ctypes.byref(shape), tp, None, None, None, None, None, None, None,
+                            ctypes.c_void_p(256), 1 << 40, None)
+    assert rc == B.H3_EINVAL
+    rc = lib.h3_routed_attn(ctypes.byref(shape), tp, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                            ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                            None, None, ctypes.c_void_p(256), 1 << 40, None)
+    assert rc == B.H3_EUNSUPPORTED   # a gate is not supported
+    hw = B.H3HeadWeights()
+    rc = lib.h3_dit_forward(ctypes.byref(shape), 1, tp, None, ctypes.byref(hw), None, None, None,
+                            None, None, None, ctypes.c_void_p(256), 1 << 40, None)
+    assert rc == B.H3_EINVAL

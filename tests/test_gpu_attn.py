@@ -1,0 +1,148 @@
+"""GPU parity of h3_routed_attn against the CPU oracle: tiny and full-size
+(15,435 rows x 40 heads x 128) workloads with a low-rank spatial field in q
+and k, the top-k rule cases, and routed-with-all-tiles equals dense."""
+import numpy as np
+import pytest
+
+from audio_diffusion_transformer_amd import synth as S
+from oracle import h3_oracle as O
+
+import gpu_harness as G
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def attn_shape(n_text, n_audio, n_video, nh, d, tile, top_k, pooled=1):
+    return S.Shape(n_text, n_audio, n_video, nh * d, nh, d, 256, tile=tile, top_k=top_k,
+                   pooled=pooled)
+
+
+def _check(sh, rows=None, seed=42, amp=1.0):
+    print(f"case: routed attn R={sh.rows} nh={sh.n_heads}x{sh.head_dim} tile={sh.tile} "
+          f"k={sh.top_k} pooled={sh.pooled}", flush=True)
+    ts, npt = S.tile_map(sh)
+    q, k, v = S.attn_qkv(sh, seed=seed, amp=amp)
+    g = G.run_routed(sh, ts, npt, q, k, v)
+    r = O.routed_attn(sh, ts, npt, q, k, v, rows=rows)
+    checked, bad, skipped = P.selection_agrees(g["sel"], r["sel"], r["scores"], npt, sh.top_k)
+    assert bad == 0 and checked >= 0.9 * (checked + skipped), (checked, bad, skipped)
+    assert np.max(np.abs(g["scores"] - r["scores"])) < 1e-3
+    got = g["out"] if rows is None else g["out"][rows]
+    m = P.metrics(got, r["out"])
+    assert m["cos"] > 0.99999 and m["rel"] < 4e-3, m
+    assert np.all(np.abs(got - r["out"]) <= 4e-3 + 2 ** -7 * np.abs(r["out"]))
+    return g, r, ts, npt, q, k, v
+
+
+def test_tiny_routed():
+    _check(attn_shape(64, 64, 896, 4, 64, 64, 4))
+
+
+def test_tiny_routed_d128_ragged():
+    _check(attn_shape(37, 91, 1001, 3, 128, 64, 5))
+
+
+def _dense_equivalent(sh, ts, npt, q, k, v):
+    """The same rows and tiles, all declared prefix: every row attends densely."""
+    shd = sh.replace(n_audio=sh.n_audio + sh.n_video, n_video=0)
+    return G.run_routed(shd, ts, len(ts) - 1, q, k, v)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_routed_with_all_tiles_equals_dense(d):
+    sh = attn_shape(40, 80, 700, 2, d, 64, 10 ** 6, pooled=0)
+    ts, npt = S.tile_map(sh)
+    q, k, v = S.attn_qkv(sh)
+    routed = G.run_routed(sh, ts, npt, q, k, v)
+    dense = _dense_equivalent(sh, ts, npt, q, k, v)
+    np.testing.assert_array_equal(routed["out_bits"], dense["out_bits"])
+
+
+def test_topk_ties_go_to_lower_tiles():
+    """q = 0: every tile score is exactly 0 on both sides, so the top-k is
+    decided by the tie rule alone: the lowest video tiles."""
+    sh = attn_shape(64, 64, 640, 2, 64, 64, 3)
+    ts, npt = S.tile_map(sh)
+    _, k, v = S.attn_qkv(sh)
+    q = np.zeros_like(k)
+    g = G.run_routed(sh, ts, npt, q, k, v)
+    r = O.routed_attn(sh, ts, npt, q, k, v)
+    np.testing.assert_array_equal(g["sel"], r["sel"])
+    assert np.all(g["sel"] == np.arange(npt, npt + 3))
+    m = P.metrics(g["out"], r["out"])
+    assert m["rel"] < 4e-3, m
+
+
+def test_topk_nan_scores_rank_last():
+    """A NaN in one key row makes that tile's mean and score NaN: the tile
+    ranks as -inf (kept only if needed) and the selection stays inside its
+    row; the oracle applies the same rule."""
+    sh = attn_shape(64, 64, 640, 2, 64, 64, 9)   # 10 video tiles, keep 9
+    ts, npt = S.tile_map(sh)
+    q, k, v = S.attn_qkv(sh)
+    k = k.copy()
+    k[0, ts[npt + 4] + 3, 5] = 0x7FC0                 # NaN in head 0, video tile 4
+    g = G.run_routed(sh, ts, npt, q, k, v)
+    r = O.routed_attn(sh, ts, npt, q, k, v)
+    assert np.all(np.isnan(g["scores"][0, :, npt + 4]))
+    np.testing.assert_array_equal(g["sel"][0], r["sel"][0])
+    assert np.all(g["sel"][0] != npt + 4)              # 9 of 10 kept: never the NaN tile
+    # the pooled branch of head 0 is NaN for every video tile (as in the oracle)
+    vid = slice(sh.n_prefix, sh.rows)
+    assert np.array_equal(np.isnan(g["out"][vid, :64]), np.isnan(r["out"][vid, :64]))
+    assert not np.isnan(g["out"][:, 64:]).any()
+
+
+def test_routed_determinism():
+    sh = attn_shape(64, 64, 896, 4, 64, 64, 4)
+    ts, npt = S.tile_map(sh)
+    q, k, v = S.attn_qkv(sh)
+    a = G.run_routed(sh, ts, npt, q, k, v)
+    b = G.run_routed(sh, ts, npt, q, k, v)
+    np.testing.assert_array_equal(a["out_bits"], b["out_bits"])
+    np.testing.assert_array_equal(a["sel"], b["sel"])
+
+
+def _sample_rows(sh, ts, npt):
+    """Rows the oracle computes one by one: ends of every segment, the first,
+    a middle and the last (ragged) video tile, rows around tile seams."""
+    R, P_ = sh.rows, sh.n_prefix
+    rows = set()
+    for a in (0, sh.n_text, P_):
+        rows.update(range(a, min(a + 3, R)))
+    for b in (sh.n_text, P_, R):
+        rows.update(range(max(b - 3, 0), b))
+    nT = len(ts) - 1
+    for t in (npt, npt + (nT - npt) // 2, nT - 1):
+        rows.update(range(ts[t], ts[t + 1]))
+    rows.update(range(ts[npt + 1] - 2, ts[npt + 1] + 2))
+    return np.array(sorted(r for r in rows if 0 <= r < R))
+
+
+FULL_ATTN = attn_shape(512, 543, 14380, 40, 128, 64, 32)
+
+
+def test_full_size_routed_sampled():
+    sh = FULL_ATTN
+    ts, npt = S.tile_map(sh)
+    _check(sh, rows=_sample_rows(sh, ts, npt))
+
+
+@pytest.mark.parametrize("tile,top_k", [(32, 8), (128, 8), (64, 8), (32, 32), (128, 32)])
+def test_full_size_sweep_sampled(tile, top_k):
+    sh = FULL_ATTN.replace(tile=tile, top_k=top_k)
+    ts, npt = S.tile_map(sh)
+    rows = _sample_rows(sh, ts, npt)[::3]
+    _check(sh, rows=rows)
+
+
+@pytest.mark.parametrize("tile", [32, 64, 128])
+def test_full_size_all_tiles_equals_dense(tile):
+    sh = FULL_ATTN.replace(tile=tile, top_k=10 ** 6, pooled=0)
+    print(f"case: full-size all-tiles vs dense, tile={tile}", flush=True)
+    ts, npt = S.tile_map(sh)
+    q, k, v = S.attn_qkv(sh)
+    routed = G.run_routed(sh, ts, npt, q, k, v)
+    dense = _dense_equivalent(sh, ts, npt, q, k, v)
+    np.testing.assert_array_equal(routed["out_bits"], dense["out_bits"])

@@ -1,0 +1,111 @@
+"""GPU parity of h3_dit_forward (blocks + final norm + heads) against the
+oracle, determinism of the forward, and the full-size block (15,435 rows,
+hidden 5,120) on sampled rows in the launch configuration the benchmark
+times."""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+from audio_diffusion_transformer_amd import binding as B
+from audio_diffusion_transformer_amd import synth as S
+from audio_diffusion_transformer_amd import tensors as T
+from oracle import h3_oracle as O
+
+import gpu_harness as G
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _forward_inputs(sh, L, seed=42):
+    ts, npt = S.tile_map(sh)
+    blocks = [S.block_weights(sh, block=l, seed=seed) for l in range(L)]
+    mods = np.stack([S.modulation(sh, block=l, seed=seed) for l in range(L)]) if L else \
+        np.zeros((0, 3, 6, sh.hidden), np.float32)
+    head = S.head_weights(sh, seed=seed)
+    mf = S.final_modulation(sh, seed=seed)
+    rope = S.rope_tables(sh)
+    x = S.activations(sh, seed=seed, field=True)
+    return ts, npt, blocks, head, mods, mf, rope, x
+
+
+def _run_forward(sh, ts, npt, blocks, head, mods, mf, rope, x):
+    shape = B.make_shape(sh, ts, npt)
+    ws = T.workspace(B.workspace_bytes(shape, ts, B.H3_WS_DIT))
+    bd = [T.weights_to_dev(b) for b in blocks]
+    hd = T.weights_to_dev(head)
+    vv = torch.empty((sh.n_video, sh.c_video), dtype=torch.float32, device="cuda")
+    va = torch.empty((sh.n_audio, sh.c_audio), dtype=torch.float32, device="cuda")
+    modd = T.to_dev(np.ascontiguousarray(mods)) if len(blocks) else None
+    B.dit_forward(shape, ts, bd, hd, modd, T.to_dev(mf), T.to_dev(rope), T.to_dev(x), vv, va, ws)
+    torch.cuda.synchronize()
+    return vv.cpu().numpy(), va.cpu().numpy()
+
+
+@pytest.mark.parametrize("L", [0, 1, 3])
+def test_tiny_forward_velocities(L):
+    sh = S.TINY
+    print(f"case: tiny forward L={L}", flush=True)
+    inp = _forward_inputs(sh, L)
+    vv, va = _run_forward(sh, *inp)
+    ts, npt, blocks, head, mods, mf, rope, x = inp
+    r = O.dit_forward(sh, ts, npt, blocks, head, mods, mf, rope, x)
+    for got, ref in ((vv, r["vel_video"]), (va, r["vel_audio"])):
+        m = P.metrics(got, ref)
+        # the stated bar is cos >= 0.998 and rel <= 0.06; a few blocks stay far inside it
+        assert m["cos"] >= 0.9999 and m["rel"] <= 5e-3, m
+
+
+def test_forward_determinism():
+    sh = S.TINY
+    inp = _forward_inputs(sh, 2)
+    a = _run_forward(sh, *inp)
+    b = _run_forward(sh, *inp)
+    ha = hashlib.sha256(a[0].tobytes() + a[1].tobytes()).hexdigest()
+    hb = hashlib.sha256(b[0].tobytes() + b[1].tobytes()).hexdigest()
+    assert ha == hb
+
+
+def test_full_size_block_sampled_rows():
+    """Hidden 5120, 40 x 128 heads, GELU FFN 20480, 15,435 rows (512 / 543 /
+    14,380), tile 64, top-k 32, pooled.  The oracle computes q, k, v and the
+    routing for every row, and attention, out projection and MLP for sampled
+    rows."""
+    sh = S.FULL
+    print("case: full-size block (oracle on sampled rows)", flush=True)
+    ts, npt = S.tile_map(sh)
+    w = S.block_weights(sh)
+    mod = S.modulation(sh)
+    rope = S.rope_tables(sh)
+    x = S.activations(sh, field=True)
+    run = G.BlockRun(sh, ts, npt, w, mod, rope, x)
+    run.run()
+    g = run.read()
+    R = sh.rows
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(510, 516), np.arange(1050, 1060),
+                                     np.arange(1055, 1055 + 64), np.arange(8000, 8070),
+                                     np.arange(R - 50, R)]))
+    print("oracle ...", flush=True)
+    r = O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows)
+    c = G.Checks("full-size block")
+    c.close("q", g["q"], r["q"], atol=2 ** -5)
+    c.close("k", g["k"], r["k"], atol=2 ** -5)
+    # K = 5120: fp32 sums and upstream flips move a product by up to ~2^-9
+    c.close("v", g["v"], r["v"], atol=2 ** -9)
+    checked, bad, skipped = P.selection_agrees(g["sel"], r["sel"], r["scores"], npt, sh.top_k)
+    c.true("sel", bad == 0 and checked >= 0.8 * (checked + skipped),
+           f"checked {checked} bad {bad} skipped {skipped}")
+    m = P.metrics(g["attn"][rows], r["attn"])
+    c.true("attn", m["cos"] > 0.99999 and m["rel"] < 4e-3, str(m))
+    for name in ("x1", "n2", "x2"):
+        c.close(name, g[name][rows], r[name], ulps=2, atol=2 ** -6, frac_1ulp=2e-2)
+    # with H = 5120 almost every row of n2 carries one 1-spacing flip, which
+    # shifts all of that row's small GELU outputs by ~1e-4: bound h by value
+    c.close("h", g["h"][rows], r["h"], ulps=2, atol=2 ** -6, frac_1ulp=0.1)
+    m = P.metrics(g["h"][rows], r["h"])
+    c.true("h metrics", m["cos"] > 0.99999 and m["rel"] < 2e-3, str(m))
+    m = P.metrics(g["x2"][rows], r["x2"])
+    c.true("x2 metrics", m["cos"] > 0.9999 and m["rel"] < 1e-3, str(m))
+    c.done()
