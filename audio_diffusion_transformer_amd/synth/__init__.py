@@ -251,3 +251,33 @@ def attn_qkv(shape: Shape, seed: int = SEED, correlated: bool = True, amp: float
         qf[h, P:] += (amp * (phi @ A[h])).astype(np.float32)
         kf[h, P:] += (amp * (phi @ B[h])).astype(np.float32)
     return f32_to_bf16(qf), f32_to_bf16(kf), v
+
+
+# ----------------------------------------------------------------------------
+# Device-side draws for large workloads (many blocks of weights)
+# ----------------------------------------------------------------------------
+
+def device_normal_bf16(name, shape, std, seed=SEED, device="cuda", mean=0.0):
+    """mean + std * N(0,1) drawn on the GPU by torch's seeded Philox generator
+    (keyed by seed and the tensor's name), rounded to bf16; returned as an
+    int16 tensor of raw bf16 bits.  Used where host generation of tens of GB
+    would dominate the run; values differ from ``normal_bf16`` of the same
+    name (another generator), the distribution is the same."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((stream_id(name) ^ (seed * 0x9E3779B97F4A7C15)) & 0x7FFFFFFFFFFFFFFF)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    t.mul_(std).add_(mean)
+    return t.to(torch.bfloat16).view(torch.int16)
+
+
+def device_block_weights(shape: Shape, block: int = 0, seed: int = SEED, std: float = 0.02,
+                         device="cuda"):
+    H, F, d = shape.hidden, shape.ffn, shape.head_dim
+    p = f"block{block}."
+    sizes = {"w_qkv": (3 * H, H), "b_qkv": (3 * H,), "w_o": (H, H), "b_o": (H,),
+             "w_fc1": (F, H), "b_fc1": (F,), "w_fc2": (H, F), "b_fc2": (H,)}
+    w = {k: device_normal_bf16(p + k, s, std, seed, device) for k, s in sizes.items()}
+    for k in ("q_gain", "k_gain"):
+        w[k] = device_normal_bf16(p + k, (d,), std, seed, device, mean=1.0)
+    return w

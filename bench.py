@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark: seconds per 50-block H3-style DiT forward at 15,435 packed rows.
+
+Workload: 50 blocks of hidden 5120, 40 heads x 128, GELU FFN 20480, 15,435
+rows (512 text / 543 audio / 14,380 video), tile 64, top-k 32 video tiles plus
+the pooled branch, random-init bf16 weights, then the final norm and the
+video / audio heads.  One "step" is one forward with that step's fresh
+modulation tables.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  Besides the time per forward it reports, for the
+dominant kernel, the achieved fraction of its roofline (algorithmic FLOP per
+launch over the launch's average duration, from HIP events recorded around
+every library kernel inside the timed region), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+N_BLOCKS = 50
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=7)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--blocks", type=int, default=N_BLOCKS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prof", action="store_true", help="time without per-kernel events")
+    return ap.parse_args()
+
+
+def kernel_work(sh, ts, npt, plan_sel_rows):
+    """Algorithmic FLOP (GEMMs, attention) and bytes (norm) per launch."""
+    R, H, F, nh, d = sh.rows, sh.hidden, sh.ffn, sh.n_heads, sh.head_dim
+    P = sh.n_prefix
+    keys = plan_sel_rows            # total keys over all query rows, per head
+    return {
+        "gemm_qkv": ("mfma", 2.0 * R * 3 * H * H),
+        "gemm_o": ("mfma", 2.0 * R * H * H),
+        "gemm_fc1": ("mfma", 2.0 * R * F * H),
+        "gemm_fc2": ("mfma", 2.0 * R * H * F),
+        "attn": ("mfma", 4.0 * d * nh * keys),
+        # modnorm: read x [R][H] bf16, write n [R][H] bf16
+        "modnorm": ("hbm", 2.0 * R * H * 2),
+    }
+
+
+def attention_keys(sh, ts, npt):
+    """sum over query rows of the number of keys each attends (one head)."""
+    lens = np.diff(ts)
+    P = sh.n_prefix
+    nQ = len(lens) - npt
+    k = min(sh.top_k, nQ)
+    # dense rows: all R keys; video rows: P prefix keys + k selected tiles.
+    # With uniform video tiles (ragged last) the selected rows are k*tile
+    # unless the ragged tile is chosen; use the mean video tile length.
+    mean_vt = float(np.mean(lens[npt:])) if nQ else 0.0
+    return P * sh.rows + sh.n_video * (P + k * mean_vt)
+
+
+def cpu_baseline(sh, ts, npt, n_blocks):
+    """The oracle (as it stands) on one full-size block: q/k/v, head layout
+    and routing over all rows, attention + out projection + MLP over a sample
+    of rows; the sampled part is scaled to all rows, then x n_blocks."""
+    from oracle import h3_oracle as O
+    from audio_diffusion_transformer_amd import synth as S
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    w = S.block_weights(sh)
+    mod = S.modulation(sh)
+    rope = S.rope_tables(sh)
+    x = S.activations(sh, field=True)
+    R = sh.rows
+    rng = np.random.default_rng(0)
+    # proportional stratified sample: text/audio and video rows in their share of R
+    n_sample = 512
+    n_dense = int(round(n_sample * sh.n_prefix / R))
+    n_vid = n_sample - n_dense
+    rows = np.sort(np.concatenate([rng.choice(sh.n_prefix, n_dense, replace=False),
+                                   sh.n_prefix + rng.choice(sh.n_video, n_vid, replace=False)]))
+    tm = {}
+    O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows, timings=tm)
+    t_all, t_rows = tm["all_rows"], tm["per_row"]
+    per_block = t_all + t_rows * R / n_sample
+    return {
+        "value": per_block * n_blocks, "unit": "s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"one block at {R} rows: norm, QKV, head layout and routing over all rows "
+                   f"({t_all:.1f} s), attention + out projection + MLP over {n_dense} text/audio "
+                   f"and {n_vid} video rows ({t_rows:.1f} s) scaled by {R}/{n_sample}; "
+                   f"per block {per_block:.1f} s, x {n_blocks} blocks (extrapolated)"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
+              f"multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from audio_diffusion_transformer_amd import binding as B
+    from audio_diffusion_transformer_amd import synth as S
+    from audio_diffusion_transformer_amd import tensors as T
+
+    sh = S.FULL
+    L = args.blocks
+    ts, npt = S.tile_map(sh)
+    shape = B.make_shape(sh, ts, npt)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    print(f"setup: {L} blocks of weights on {torch.cuda.get_device_name(0)}", file=sys.stderr,
+          flush=True)
+    blocks = [S.device_block_weights(sh, block=l) for l in range(L)]
+    warr = (B.H3BlockWeights * L)(*[B.block_weights_struct(b) for b in blocks])
+    heads = {k: T.to_dev(v) for k, v in S.head_weights(sh).items()}
+    hw = B.head_weights_struct(heads)
+    n_fwd = args.warmup + args.steps
+    mods = [T.to_dev(np.stack([S.modulation(sh, block=l, step=s) for l in range(L)]))
+            for s in range(n_fwd)]
+    mfin = [T.to_dev(S.final_modulation(sh, step=s)) for s in range(n_fwd)]
+    rope = T.to_dev(S.rope_tables(sh))
+    x = T.to_dev(S.activations(sh, field=True))
+    vv = torch.empty((sh.n_video, sh.c_video), dtype=torch.float32, device=dev)
+    va = torch.empty((sh.n_audio, sh.c_audio), dtype=torch.float32, device=dev)
+    ws = T.workspace(B.workspace_bytes(shape, ts, B.H3_WS_DIT))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print("setup done", file=sys.stderr, flush=True)
+
+    def forward(s):
+        B.dit_forward(shape, ts, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws, stream=stream)
+
+    for s in range(args.warmup):
+        forward(s)
+    torch.cuda.synchronize()
+    print(f"warmup done ({args.warmup})", file=sys.stderr, flush=True)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    if not args.no_prof:
+        B.prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        forward(args.warmup + i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = B.prof_read() if not args.no_prof else {}
+    B.prof_enable(False)
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    print(f"timed {args.steps} forwards: {ms_per_step:.1f} ms each", file=sys.stderr, flush=True)
+
+    # ---- per-kernel roofline from the events of the timed region ----
+    work = kernel_work(sh, ts, npt, attention_keys(sh, ts, npt))
+    kernels = {}
+    for name, (n, ms) in kern.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        entry = {"launches": n, "avg_ms": round(avg, 4), "total_ms": round(ms, 2)}
+        if name in work:
+            kind, amount = work[name]
+            if kind == "mfma":
+                ach = amount / (avg * 1e-3) / 1e12
+                entry.update(achieved_tflops=round(ach, 1), frac=round(ach / PEAK_BF16_TFLOPS, 4))
+            else:
+                ach = amount / (avg * 1e-3) / 1e9
+                entry.update(achieved_gbs=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 4))
+        kernels[name] = entry
+    roofline = None
+    if kernels:
+        dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["total_ms"])
+        kind, amount = work[dom]
+        e = kernels[dom]
+        if kind == "mfma":
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": e["achieved_tflops"],
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": e["frac"],
+                        "traffic": None}
+        else:
+            roofline = {"bound": "hbm", "kernel": dom, "achieved": e["achieved_gbs"],
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": e["frac"],
+                        "traffic": None}
+        gemm_flop = sum(work[k][1] * kernels[k]["launches"] for k in kernels
+                        if k.startswith("gemm_"))
+        gemm_ms = sum(kernels[k]["total_ms"] for k in kernels if k.startswith("gemm_"))
+        roofline["gemm_all_frac"] = round(gemm_flop / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+
+    srt = sorted(step_ms)
+    line = {
+        "metric": "s per 50-block DiT forward at 15,435 rows; GEMM/attn % of bf16 MFMA peak",
+        "value": round(ms_per_step / 1e3, 5),
+        "unit": "s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"{L}-block H3-style DiT forward, 15,435 rows (512 text / 543 "
+                                f"audio / 14,380 video), hidden 5120, 40x128 heads, GELU FFN "
+                                f"20480, tile 64, top-k 32 + pooled, heads 96/32, seeded "
+                                f"random bf16 weights"),
+                   "blocks": L, "rows": sh.rows, "hidden": sh.hidden, "ffn": sh.ffn,
+                   "tile": sh.tile, "top_k": sh.top_k},
+        "step_ms": [round(s, 2) for s in step_ms],
+        "median_step_s": round(srt[len(srt) // 2] / 1e3, 5),
+        "roofline": roofline,
+        "kernels": kernels,
+        "prof_events": not args.no_prof,
+    }
+    if not args.no_cpu_baseline:
+        print("cpu baseline (oracle on a bounded sample) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(sh, ts, npt, L)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

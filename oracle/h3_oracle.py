@@ -43,6 +43,8 @@ invariants, library routines and brute force.
 """
 from __future__ import annotations
 
+import time
+
 import numpy as np
 from scipy.special import erf as _erf
 
@@ -294,7 +296,8 @@ def attention(q, k, v, tile_start, n_prefix_tiles, n_prefix_rows, rt, use_pooled
     return out
 
 
-def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=None):
+def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=None,
+                  timings=None):
     """One DiT block, steps in the order of TensorFold PR #949 "What it adds"
     (block.zig) with the GELU MLP of the workload description:
 
@@ -311,7 +314,10 @@ def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=N
     mod: fp32 [3][6][H].  rope: fp32 [R][d/2][2] or None.  x_in: bf16 bits.
     out_rows: None for all rows, else the rows whose attention / x1 / x2 are
     computed (q, k, v and routing always cover all rows).
+    timings: None, or a dict that receives the wall time of the all-row part
+    ("all_rows") and of the per-row part ("per_row").
     Returns a dict of float64 intermediates (bf16 values where rounded)."""
+    t0 = time.perf_counter()
     seg = row_segments(sh.n_text, sh.n_audio, sh.n_video)
     P = sh.n_text + sh.n_audio
     ts = check_tile_map(tile_start, sh.n_text, sh.n_audio, sh.n_video, n_prefix_tiles)
@@ -328,6 +334,7 @@ def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=N
     kt = qk_norm_rope(k, f["k_gain"], rope, eps)
     rt = routing(qt, kt, v, ts, n_prefix_tiles, sh.top_k)
     rows = np.arange(x.shape[0]) if out_rows is None else np.asarray(out_rows)
+    t1 = time.perf_counter()
     a = round_bf16(attention(qt, kt, v, ts, n_prefix_tiles, P, rt, bool(sh.pooled), rows))
     sr = seg[rows]
     o = round_bf16(linear(a, f["w_o"], f["b_o"]))
@@ -336,6 +343,9 @@ def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=N
     hdn = round_bf16(gelu(linear(n2, f["w_fc1"], f["b_fc1"])))
     ff = round_bf16(linear(hdn, f["w_fc2"], f["b_fc2"]))
     x2 = round_bf16(x1 + gate2[sr] * ff)
+    if timings is not None:
+        timings["all_rows"] = t1 - t0
+        timings["per_row"] = time.perf_counter() - t1
     return dict(rows=rows, n1=n1, y=y, q=qt, k=kt, v=v, attn=a, o=o, x1=x1, n2=n2, h=hdn,
                 f=ff, x2=x2, **rt)
 
