@@ -72,6 +72,9 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
       return fail(H3_EUNSUPPORTED, "hidden %d must be a multiple of 256 and <= 8192", p.H);
     if (s->ffn < 256 || s->ffn % 256 != 0)
       return fail(H3_EUNSUPPORTED, "ffn %d must be a positive multiple of 256", s->ffn);
+    if (!gemm_shape_ok(p.R, 3 * p.H, p.H) || !gemm_shape_ok(p.R, s->ffn, p.H) ||
+        !gemm_shape_ok(p.R, p.H, s->ffn))
+      return fail(H3_EUNSUPPORTED, "rows x width too large for the GEMM (R*F must stay below 2^31)");
   } else {
     p.H = p.nh * p.D;
   }

@@ -3,21 +3,30 @@
 // These are the block's four products (TensorFold PR #949, "What it adds":
 // q/k/v products, out projection, MLP in / out; "Precision": bf16 operands,
 // fp32 sums).  Both operands are K-contiguous ([row][K] activations, [out][in]
-// weights), which is exactly the per-lane operand order of the CDNA4 MFMA:
+// weights), which is the per-lane operand order of the CDNA4 MFMA:
 // v_mfma_f32_32x32x16_bf16 takes 8 consecutive K elements of one A row and of
 // one B row per lane.
 //
-// Tiling: a 256-thread workgroup (4 wave64) owns a 256x256 C tile; each wave
-// owns a 128x128 quadrant as 4x4 MFMA blocks of 32x32 (256 fp32 accumulators
-// per lane).  K advances 64 at a time through two LDS stages (rows padded to
-// 72 bf16 = 144 B so the 16-byte fragment reads of 8 consecutive rows hit
-// distinct banks); the next stage's global loads are issued before the MFMAs
-// of the current one.  Workgroup ids are remapped so that each XCD (ids are
-// dealt round-robin over the 8 XCDs) works on a contiguous band of tiles, and
-// within a band tiles are walked in groups of 8 tile-rows for L2 reuse.
+// Tiling: a 512-thread workgroup (8 wave64, two per SIMD) owns a 256x256 C
+// tile; wave w owns the 128x64 sub-tile (w/4, w%4) as 4x2 MFMA blocks of 32x32
+// (128 fp32 accumulators per lane).  K advances 64 at a time through a
+// two-stage LDS ring filled by global_load_lds_dwordx4: each lane's 16 bytes
+// go straight to LDS, so no registers hold staged tiles.  A stage row is one
+// full 128-byte line of A or B; its eight 16-byte chunks are stored XOR-
+// swizzled by (row / 2) % 8, which makes the fragment reads (16 consecutive
+// rows, same chunk) hit 16 distinct bank groups.  The loads of stage k+1 are
+// issued right after the barrier that opens stage k.  The loads are issued as
+// inline assembly so that the compiler does not insert its own conservative
+// waits for them; this kernel waits on vmcnt itself.
 //
-// Epilogues (rounding points of the block, h3.c README on rounded bf16
-// residuals):
+// Workgroup ids are remapped so that each XCD (ids are dealt round-robin over
+// the 8 XCDs) works on a contiguous band of tiles; within a band tiles are
+// walked in groups of 8 tile-rows so that concurrent tiles share A and B
+// panels in that XCD's L2.
+//
+// Epilogues (rounding points of the block; h3.c README on rounded bf16
+// residuals).  The bf16 tile is staged through LDS so that residual loads and
+// output stores are 16-byte coalesced:
 //   EPI_BIAS:         C = bf(acc + bias)
 //   EPI_BIAS_GELU:    C = bf(gelu(acc + bias)),  gelu(z) = z/2 (1 + erf(z/sqrt2))
 //   EPI_BIAS_RESGATE: C = bf(res + gate[seg(row)] * bf(acc + bias))
@@ -29,42 +38,44 @@ namespace h3 {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row
+constexpr int STAGE = BM * BK;  // bf16 elements of one operand in one stage (32 KB)
+
+// s_waitcnt immediate that waits for vmcnt <= n and leaves expcnt and lgkmcnt
+// unchecked (gfx9 encoding: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+#define H3_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t*)p;
+}
+
+// 16 bytes per lane from gptr into LDS at (m0 + 16 * lane).  M0 is a reserved
+// register that the compiler does not allocate (gfx9+ LDS instructions do not
+// read it), so setting it here disturbs no compiler-managed value.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
 
 __device__ __forceinline__ int seg_of(int row, int n_text, int n_prefix) {
   return row < n_text ? 0 : (row < n_prefix ? 1 : 2);
 }
 
-__device__ __forceinline__ void gload8(u32x4_t (&ra)[8], u32x4_t (&rb)[8], const bf16_t* A,
-                                       const bf16_t* B, const int (&oa)[8], const int (&ob)[8],
-                                       int k0) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ra[i] = *reinterpret_cast<const u32x4_t*>(A + oa[i] + k0);
-    rb[i] = *reinterpret_cast<const u32x4_t*>(B + ob[i] + k0);
-  }
-}
-
-__device__ __forceinline__ void lstore8(bf16_t* sa, bf16_t* sb, const u32x4_t (&ra)[8],
-                                        const u32x4_t (&rb)[8], int lrow, int lseg) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    *reinterpret_cast<u32x4_t*>(&sa[(lrow + 32 * i) * LDS_STRIDE + lseg * 8]) = ra[i];
-    *reinterpret_cast<u32x4_t*>(&sb[(lrow + 32 * i) * LDS_STRIDE + lseg * 8]) = rb[i];
-  }
-}
-
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16_t* __restrict__ A,
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__ A,
                                                       const bf16_t* __restrict__ B, int M,
                                                       int N, int K, GemmEpi ep) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDS_STRIDE];
+  // two stages of A then B; reused whole (128 KB) by the epilogue
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * STAGE];
+  bf16_t* const sA0 = smem;
+  bf16_t* const sB0 = smem + STAGE;
+  bf16_t* const sA1 = smem + 2 * STAGE;
+  bf16_t* const sB1 = smem + 3 * STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
-
-  // XCD-aware id: XCD x receives ids x, x+8, ...; give it a contiguous range.
   const int nb = gridDim.x, bid = blockIdx.x;
   const int q8 = nb >> 3, r8 = nb & 7, xcd = bid & 7, idx = bid >> 3;
   const int lin = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
@@ -76,102 +87,132 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(const bf16_t* __restrict__
   const int tm = first_m + (lin % per_group) % gsize;
   const int tn = (lin % per_group) / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // Global -> LDS copy: thread t moves rows t/8 + 32 i (i < 8), 16 bytes at
-  // column (t % 8) * 8 of the current 64-wide K slab, for A and for B.
-  const int lrow = tid >> 3, lseg = tid & 7;
-  int oa[8], ob[8];  // element offsets (M*K and N*K stay below 2^31)
+  // DMA: a stage is 256 rows x 8 chunks per operand; instruction i of wave w
+  // fills LDS chunks [(8i + w) * 64, +64), i.e. 8 rows.
+  int ga[4], gb[4], la[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ra = min(m0 + lrow + 32 * i, M - 1);  // ragged M: clamp, result rows dropped
-    oa[i] = ra * K + lseg * 8;
-    ob[i] = (n0 + lrow + 32 * i) * K + lseg * 8;
+  for (int i = 0; i < 4; ++i) {
+    const int q = (i * 8 + wave) * 64 + lane;
+    const int r = q >> 3, c = q & 7, gc = c ^ swz(r);
+    ga[i] = min(m0 + r, M - 1) * K + gc * 8;  // ragged M: clamp; rows >= M are dropped
+    gb[i] = (n0 + r) * K + gc * 8;
+    la[i] = (i * 8 + wave) * 64 * 8;
   }
-  const int wm = wave >> 1, wn = wave & 1;
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
+  auto issue = [&](bf16_t* sa, bf16_t* sb, int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dma16(A + ga[i] + k0, lds_addr(sa + la[i]));
+      dma16(B + gb[i] + k0, lds_addr(sb + la[i]));
+    }
+  };
 
-  f32x16_t acc[4][4];
+  const int lr = lane & 31, half = lane >> 5;
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int KT = K / BK;
-  {
-    u32x4_t ra[8], rb[8];
-    gload8(ra, rb, A, B, oa, ob, 0);
-    lstore8(sA[0], sB[0], ra, rb, lrow, lseg);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < KT;
-    u32x4_t ra[8], rb[8];
-    if (more) gload8(ra, rb, A, B, oa, ob, (kt + 1) * BK);
-    const bf16_t* a_base = &sA[buf][(wm * 128 + frow) * LDS_STRIDE + fk];
-    const bf16_t* b_base = &sB[buf][(wn * 128 + frow) * LDS_STRIDE + fk];
+  auto compute = [&](const bf16_t* sa, const bf16_t* sb) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[4], bfr[4];
+      const int gc = kk * 2 + half;
+      bf16x8_t af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + lr;
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + r * BK + (gc ^ swz(r)) * 8));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + lr;
+        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + r * BK + (gc ^ swz(r)) * 8));
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(a_base + i * 32 * LDS_STRIDE + kk * 16));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(b_base + j * 32 * LDS_STRIDE + kk * 16));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (more) lstore8(sA[buf ^ 1], sB[buf ^ 1], ra, rb, lrow, lseg);
-    __syncthreads();
-  }
+  };
 
-  // Epilogue.  Accumulator element e of block (i, j) in lane l sits at
-  // row 8(e/4) + 4(l/32) + e%4, column l%32 of that 32x32 block.
+  const int KT = K / BK;  // even (K % 128 == 0)
+  issue(sA0, sB0, 0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    // stage 0 holds slice kt: wait for this thread's loads, then everyone's
+    __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + 1 < KT) issue(sA1, sB1, (kt + 1) * BK);
+    compute(sA0, sB0);
+    __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + 2 < KT) issue(sA0, sB0, (kt + 2) * BK);
+    compute(sA1, sB1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- epilogue ----
+  // Accumulator element e of block (i, j) in lane l sits at row 8(e/4) + 4(l/32)
+  // + e%4, column l%32 of that 32x32 block.  Each wave rounds its 128x64
+  // sub-tile into its own 16 KB of LDS, then writes it back in 16-byte chunks.
+  bf16_t* st = smem + wave * (128 * 64);
   const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = n0 + wn * 128 + j * 32 + col_l;
-    const float bias = bf2f(ep.bias[col]);
+  for (int j = 0; j < 2; ++j) {
+    const float bias = bf2f(ep.bias[n0 + wn * 64 + j * 32 + col_l]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + row_l + (e & 3);
-        if (row >= M) continue;
-        const float v = acc[i][j][e] + bias;
-        const size_t o = (size_t)row * N + col;
-        if constexpr (EPI == EPI_BIAS) {
-          ep.out[o] = f2bf(v);
-        } else if constexpr (EPI == EPI_BIAS_GELU) {
-          ep.out[o] = f2bf(0.5f * v * (1.0f + erff(v * 0.70710678118654752f)));
-        } else {
-          const float ob = bf2f(f2bf(v));
-          const int sg = seg_of(row, ep.n_text, ep.n_prefix);
-          const float gv = ep.gate[(size_t)sg * ep.gate_seg_stride + col];
-          ep.out[o] = f2bf(fmaf(gv, ob, bf2f(ep.res[o])));
-        }
+        const int r = i * 32 + 8 * (e >> 2) + row_l + (e & 3);
+        float v = acc[i][j][e] + bias;
+        if constexpr (EPI == EPI_BIAS_GELU) v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+        st[r * 64 + j * 32 + col_l] = f2bf(v);
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+  for (int t = 0; t < 16; ++t) {
+    const int q = t * 64 + lane;
+    const int r = q >> 3, c8 = (q & 7) * 8;
+    const int row = m0 + wm * 128 + r;
+    if (row >= M) continue;
+    const int col = n0 + wn * 64 + c8;
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + r * 64 + c8);
+    const size_t o = (size_t)row * N + col;
+    if constexpr (EPI == EPI_BIAS_RESGATE) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ep.res + o);
+      const float* gp =
+          ep.gate + (size_t)seg_of(row, ep.n_text, ep.n_prefix) * ep.gate_seg_stride + col;
+      const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
+      const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gp + 4);
+      const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2)
+        v[t2] = pack2(fmaf(gv[2 * t2], bflo(v[t2]), bflo(x[t2])),
+                      fmaf(gv[2 * t2 + 1], bfhi(v[t2]), bfhi(x[t2])));
     }
+    *reinterpret_cast<u32x4_t*>(ep.out + o) = v;
   }
 }
 
 }  // namespace
 
 bool gemm_shape_ok(int M, int N, int K) {
-  return M >= 1 && N >= BN && N % BN == 0 && K >= BK && K % BK == 0;
+  return M >= 1 && N >= BN && N % BN == 0 && K >= 2 * BK && K % (2 * BK) == 0 &&
+         (long long)M * K < (1ll << 31) && (long long)N * K < (1ll << 31);
 }
 
 hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, int K,
                        const GemmEpi& ep, hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  dim3 grid(tiles), block(256);
+  dim3 grid(tiles), block(512);
   switch (epi) {
     case EPI_BIAS:
       hipLaunchKernelGGL(k_gemm_bf16<EPI_BIAS>, grid, block, 0, s, A, B, M, N, K, ep);
