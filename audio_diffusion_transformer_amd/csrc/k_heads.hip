@@ -12,7 +12,8 @@
 //   u~ = bf( rope( u * (sum u^2 / D + eps)^-1/2 * gain ) )
 //   rope: (a, b) -> (a cos - b sin, b cos + a sin),  cos/sin from the caller's table
 // v is copied unchanged and written transposed (v^T [nh][D][Rp]) through LDS, so
-// that the attention kernel reads runs of consecutive keys per head dimension.
+// that the attention kernel reads runs of keys per head dimension; within each
+// aligned 16-row group the middle two 4-row blocks are swapped (see below).
 // Padded rows (beyond a tile's length, up to the next multiple of 32) are
 // written as zeros.  Tile sums of q~, k~ and v are kept in fp32 per lane, then
 // combined across the waves in a fixed order and divided by the tile's true
@@ -134,13 +135,18 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
       }
     }
     __syncthreads();
-    // v^T: thread -> (dimension c, 4 consecutive rows)
+    // v^T: thread -> (dimension c, 4 consecutive rows).  Within every aligned
+    // group of 16 rows the 4-row blocks are stored in the order 0, 2, 1, 3, so
+    // that the 8 keys one lane feeds to the value-product MFMA (rows 4g..4g+3
+    // and 8+4g..8+4g+3 of a 16-row group) are 16 contiguous bytes.
     for (int idx = tid; idx < D * 8; idx += 256) {
       const int c = idx >> 3, r4 = (idx & 7) * 4;
       u32x2_t w;
       w[0] = (uint32_t)sV[(r4 + 0) * SV + c] | ((uint32_t)sV[(r4 + 1) * SV + c] << 16);
       w[1] = (uint32_t)sV[(r4 + 2) * SV + c] | ((uint32_t)sV[(r4 + 3) * SV + c] << 16);
-      *reinterpret_cast<u32x2_t*>(a.vt + ((size_t)h * D + c) * a.Rp + ps + c0 + r4) = w;
+      const int blk = (r4 >> 2) & 3;
+      const int pos = (r4 & ~12) | (((blk == 1) ? 2 : (blk == 2) ? 1 : blk) << 2);
+      *reinterpret_cast<u32x2_t*>(a.vt + ((size_t)h * D + c) * a.Rp + ps + c0 + pos) = w;
     }
     __syncthreads();
   }

@@ -55,7 +55,8 @@ enum {
   H3_EINVAL = -1,       /* bad shape, tile map or null required pointer */
   H3_EWORKSPACE = -2,   /* ws_bytes smaller than h3_workspace_bytes() */
   H3_EHIP = -3,         /* a HIP launch or runtime error */
-  H3_EUNSUPPORTED = -4  /* valid but not supported (e.g. head_dim not 64/128) */
+  H3_EUNSUPPORTED = -4  /* valid but not supported: head_dim not 64/128, more than 2048 tiles,
+                           more than 512 selected tiles, padded rows above 131072 */
 };
 
 enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2 };
@@ -67,8 +68,9 @@ typedef struct {
   int32_t hidden;                    /* H = n_heads * head_dim; multiple of 256, <= 8192 */
   int32_t n_heads, head_dim;         /* head_dim in {64, 128} */
   int32_t ffn;                       /* F, multiple of 256 */
-  int32_t n_tiles, n_prefix_tiles;   /* tile map size; prefix tiles cover rows [0, P) */
-  int32_t top_k;                     /* video key tiles per (head, video query tile); >= nQ keeps all */
+  int32_t n_tiles, n_prefix_tiles;   /* tile map size (<= 2048); prefix tiles cover rows [0, P) */
+  int32_t top_k;                     /* video key tiles per (head, video query tile); >= nQ keeps all;
+                                        min(top_k, nQ) <= 512 */
   int32_t pooled;                    /* 1: add the pooled branch to video rows */
   float norm_eps;                    /* eps of the RMS norms (activation and Q/K) */
 } h3_shape;

@@ -14,6 +14,14 @@ def b2f(u):
     return T.bf16_bits_to_f64(u)
 
 
+def vt_key_order(vt):
+    """v^T is stored with the middle two 4-row blocks of every 16-row group
+    swapped (an involution); undo it: [..., Rp] -> rows in order."""
+    sh = vt.shape
+    x = vt.reshape(sh[:-1] + (sh[-1] // 16, 4, 4))
+    return np.ascontiguousarray(x[..., [0, 2, 1, 3], :]).reshape(sh)
+
+
 class BlockRun:
     """One h3_block_forward call; intermediates read back from the workspace."""
 
@@ -48,10 +56,11 @@ class BlockRun:
         r = {}
         r["q"] = P.unpad_rows(b2f(view(lay.q, np.uint16, (nh, Rp, d))), ts, tp)
         r["k"] = P.unpad_rows(b2f(view(lay.k, np.uint16, (nh, Rp, d))), ts, tp)
-        vt = b2f(view(lay.vt, np.uint16, (nh, d, Rp)))
+        vt_bits = vt_key_order(view(lay.vt, np.uint16, (nh, d, Rp)))
+        vt = b2f(vt_bits)
         r["v"] = P.unpad_rows(np.swapaxes(vt, 1, 2), ts, tp)
         r["q_pad"] = view(lay.q, np.uint16, (nh, Rp, d))
-        r["vt_pad"] = view(lay.vt, np.uint16, (nh, d, Rp))
+        r["vt_pad"] = vt_bits
         r["qbar"] = view(lay.qbar, np.float32, (nh, nQ, d)).astype(np.float64)
         r["kbar"] = view(lay.kbar, np.float32, (nh, nT, d)).astype(np.float64)
         r["vbar"] = view(lay.vbar, np.float32, (nh, nT, d)).astype(np.float64)
