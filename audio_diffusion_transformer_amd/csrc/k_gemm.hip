@@ -14,10 +14,19 @@
 // go straight to LDS, so no registers hold staged tiles.  A stage row is one
 // full 128-byte line of A or B; its eight 16-byte chunks are stored XOR-
 // swizzled by (row / 2) % 8, which makes the fragment reads (16 consecutive
-// rows, same chunk) hit 16 distinct bank groups.  The loads of stage k+1 are
-// issued right after the barrier that opens stage k.  The loads are issued as
-// inline assembly so that the compiler does not insert its own conservative
-// waits for them; this kernel waits on vmcnt itself.
+// rows, same chunk) hit 16 distinct bank groups.
+//
+// Schedule (ping-pong): waves w and w + 4 share a SIMD.  Waves 0-3 and 4-7
+// run the same sequence of phases one phase apart, so that while one wave of
+// a SIMD runs its MFMA phase (16 products, half a stage) the other issues its
+// memory phase (fragment reads for its next MFMA phase and, once per stage,
+// its share of the next stage's loads).  All eight waves meet at a barrier
+// between phases.  The loads of stage s+1 go into the buffer that stage s-1
+// used; they are issued in the first memory phase of stage s and waited for
+// before the barrier that precedes the first read of stage s+1.  The loads
+// are issued as inline assembly (scalar base address, per-lane 32-bit
+// offsets) so that the compiler does not insert its own conservative waits
+// for them; this kernel waits on vmcnt itself.
 //
 // Workgroup ids are remapped so that each XCD (ids are dealt round-robin over
 // the 8 XCDs) works on a contiguous band of tiles; within a band tiles are
@@ -28,7 +37,7 @@
 // residuals).  The bf16 tile is staged through LDS so that residual loads and
 // output stores are 16-byte coalesced:
 //   EPI_BIAS:         C = bf(acc + bias)
-//   EPI_BIAS_GELU:    C = bf(gelu(acc + bias)),  gelu(z) = z/2 (1 + erf(z/sqrt2))
+//   EPI_BIAS_GELU:    C = bf(gelu(acc + bias)),  gelu(z) = z/2 (1 + erf(z/sqrt2)) (gelu_erf below)
 //   EPI_BIAS_RESGATE: C = bf(res + gate[seg(row)] * bf(acc + bias))
 #include "common.h"
 #include "internal.h"
@@ -43,6 +52,8 @@ constexpr int STAGE = BM * BK;  // bf16 elements of one operand in one stage (32
 // s_waitcnt immediate that waits for vmcnt <= n and leaves expcnt and lgkmcnt
 // unchecked (gfx9 encoding: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 #define H3_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+// s_waitcnt immediate that waits for lgkmcnt == 0 only
+#define H3_LGKMCNT0 0xC07F
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
@@ -50,13 +61,47 @@ __device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t*)p;
 }
 
-// 16 bytes per lane from gptr into LDS at (m0 + 16 * lane).  M0 is a reserved
-// register that the compiler does not allocate (gfx9+ LDS instructions do not
-// read it), so setting it here disturbs no compiler-managed value.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
-               "s"(__builtin_amdgcn_readfirstlane(lds))
+// 16 bytes per lane from (sbase + voff) into LDS at (m0 + 16 * lane): sbase a
+// wave-uniform address in SGPRs, voff a per-lane byte offset.  M0 is a
+// reserved register that the compiler does not allocate (gfx9+ LDS
+// instructions do not read it), so setting it here disturbs no
+// compiler-managed value.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds)
                : "memory");
+}
+
+// A wave-uniform pointer moved into SGPRs (the builtin returns int: widen
+// through uint32_t, never by sign extension).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// GELU z * Phi(z), Phi(z) = (1 + erf(z / sqrt2)) / 2, with erfc(x), x >= 0, from
+// Abramowitz & Stegun 7.1.26: erfc(x) = (a1 t + ... + a5 t^5) e^(-x^2),
+// t = 1 / (1 + p x), |error| <= 1.5e-7.  Phi(z) = 1 - erfc(x)/2 for z >= 0 and
+// erfc(x)/2 for z < 0 (x = |z| / sqrt2), so the negative tail is computed
+// without cancellation.  Straight-line code: one reciprocal, one exp2.
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  const float q = p * t * __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);  // erfc(x)
+  const float phi = z >= 0.f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
+  return z * phi;
 }
 
 __device__ __forceinline__ int seg_of(int row, int n_text, int n_prefix) {
@@ -67,12 +112,8 @@ template <int EPI>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__ A,
                                                       const bf16_t* __restrict__ B, int M,
                                                       int N, int K, GemmEpi ep) {
-  // two stages of A then B; reused whole (128 KB) by the epilogue
+  // two stages of (A, B); reused whole (128 KB) by the epilogue
   __shared__ __attribute__((aligned(16))) bf16_t smem[4 * STAGE];
-  bf16_t* const sA0 = smem;
-  bf16_t* const sB0 = smem + STAGE;
-  bf16_t* const sA1 = smem + 2 * STAGE;
-  bf16_t* const sB1 = smem + 3 * STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
@@ -87,24 +128,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
   const int tm = first_m + (lin % per_group) % gsize;
   const int tn = (lin % per_group) / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int grp = wave >> 2, wm = wave >> 2, wn = wave & 3;
 
-  // DMA: a stage is 256 rows x 8 chunks per operand; instruction i of wave w
-  // fills LDS chunks [(8i + w) * 64, +64), i.e. 8 rows.
-  int ga[4], gb[4], la[4];
+  // Loads: a stage is 256 rows x 8 chunks per operand; thread t moves chunks
+  // 512 i + t (i < 4) of A and of B.  Byte offsets from the stage's column.
+  uint32_t ga[4], gb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = (i * 8 + wave) * 64 + lane;
-    const int r = q >> 3, c = q & 7, gc = c ^ swz(r);
-    ga[i] = min(m0 + r, M - 1) * K + gc * 8;  // ragged M: clamp; rows >= M are dropped
-    gb[i] = (n0 + r) * K + gc * 8;
-    la[i] = (i * 8 + wave) * 64 * 8;
+    const int q = i * 512 + tid;
+    const int r = q >> 3, gc = (q & 7) ^ swz(r);
+    ga[i] = 2u * (uint32_t)(min(m0 + r, M - 1) * K + gc * 8);  // ragged M: clamp; rows >= M are dropped
+    gb[i] = 2u * (uint32_t)((n0 + r) * K + gc * 8);
   }
-  auto issue = [&](bf16_t* sa, bf16_t* sb, int k0) {
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 64 * 16);
+  auto issue = [&](int s) {
+    const void* pa = uniform_ptr(A + s * BK);
+    const void* pb = uniform_ptr(B + s * BK);
+    const uint32_t l = lds0 + (uint32_t)((s & 1) * 2 * STAGE * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dma16(A + ga[i] + k0, lds_addr(sa + la[i]));
-      dma16(B + gb[i] + k0, lds_addr(sb + la[i]));
+      dma16(pa, ga[i], l + i * 512 * 16);
+      dma16(pb, gb[i], l + STAGE * 2 + i * 512 * 16);
     }
   };
 
@@ -117,42 +161,58 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  auto compute = [&](const bf16_t* sa, const bf16_t* sb) {
+  // fragments of half a stage (k-steps 2 hs, 2 hs + 1): A rows wm*128 + 32i + l%32,
+  // B rows wn*64 + 32j + l%32, k = 16 kk + 8 (l / 32) .. + 7
+  bf16x8_t fa[2][4], fb[2][2];
+  auto read_frags = [&](int s, int hs) {
+    const bf16_t* sa = smem + (s & 1) * 2 * STAGE;
+    const bf16_t* sb = sa + STAGE;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int gc = kk * 2 + half;
-      bf16x8_t af[4], bfr[2];
+    for (int kk = 0; kk < 2; ++kk) {
+      const int gc = (hs * 2 + kk) * 2 + half;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wm * 128 + i * 32 + lr;
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + r * BK + (gc ^ swz(r)) * 8));
+        fa[kk][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + r * BK + (gc ^ swz(r)) * 8));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = wn * 64 + j * 32 + lr;
-        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + r * BK + (gc ^ swz(r)) * 8));
+        fb[kk][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + r * BK + (gc ^ swz(r)) * 8));
       }
+    }
+  };
+  auto products = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
   };
 
-  const int KT = K / BK;  // even (K % 128 == 0)
-  issue(sA0, sB0, 0);
-  for (int kt = 0; kt < KT; kt += 2) {
-    // stage 0 holds slice kt: wait for this thread's loads, then everyone's
-    __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
-    asm volatile("s_barrier" ::: "memory");
-    if (kt + 1 < KT) issue(sA1, sB1, (kt + 1) * BK);
-    compute(sA0, sB0);
-    __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
-    asm volatile("s_barrier" ::: "memory");
-    if (kt + 2 < KT) issue(sA0, sB0, (kt + 2) * BK);
-    compute(sA1, sB1);
+  const int KT = K / BK;  // >= 2
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+  phase_barrier();
+  if (grp == 1) phase_barrier();  // the second group runs one phase behind
+  for (int s = 0; s < KT; ++s) {
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      // memory phase
+      if (hs == 0 && s + 1 < KT) issue(s + 1);
+      read_frags(s, hs);
+      __builtin_amdgcn_s_waitcnt(H3_LGKMCNT0);
+      if (grp == 1 && hs == 1 && s + 1 < KT) __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+      phase_barrier();
+      // MFMA phase
+      products();
+      if (grp == 0 && hs == 1 && s + 1 < KT) __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+      phase_barrier();
+    }
   }
+  if (grp == 0) phase_barrier();
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -171,7 +231,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
       for (int e = 0; e < 16; ++e) {
         const int r = i * 32 + 8 * (e >> 2) + row_l + (e & 3);
         float v = acc[i][j][e] + bias;
-        if constexpr (EPI == EPI_BIAS_GELU) v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+        if constexpr (EPI == EPI_BIAS_GELU) v = gelu_erf(v);
         st[r * 64 + j * 32 + col_l] = f2bf(v);
       }
   }
