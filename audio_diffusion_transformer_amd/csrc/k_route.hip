@@ -6,15 +6,19 @@
 // "Kernel contract" (top-k rule: a NaN score ranks as -inf, ties go to the
 // lower tile).
 //
-// One wave per (head, video query tile), four per workgroup.
-//   S[j]   = (qbar . kbar_j) * D^-1/2          for every key tile j (fp32)
+// One wave per (head, video query tile); a workgroup takes 8 query tiles of one
+// head, so the head's key-tile means are staged through LDS once for 8 waves.
+//   S[j]   = (qbar . kbar_j) * D^-1/2          for every key tile j (fp32, c ascending)
 //   sel    = the top_k video tiles by (S, lower j first), written ascending
 //   pooled = sum_j exp(S_j - max S) vbar_j / sum_j exp(S_j - max S)   over all key tiles
-// Top-k is a repeated wave-wide argmax over 64-bit keys: the high word is the
-// score mapped to an order-preserving unsigned integer (NaN -> -inf, -0 -> +0),
-// the low word is the inverted tile id, so the larger key is the larger score
-// and, between equal scores, the lower tile.  The k winners are then placed in
-// ascending order by counting.
+// Lane l holds the scores of tiles l, l + 64, ...  Top-k is a radix select
+// over 64-bit keys: the high word is the score mapped to an order-preserving
+// unsigned integer (NaN -> -inf, -0 -> +0), the low word the inverted tile id,
+// so the larger key is the larger score and, between equal scores, the lower
+// tile; keys are distinct.  The k-th largest key T is found bit by bit from
+// the top (a candidate bit stays set when at least k keys are >= the
+// candidate, counted with wave ballots), and the selected tiles are exactly
+// the keys >= T, written in ascending tile order from the ballot masks.
 #include "common.h"
 #include "internal.h"
 
@@ -22,8 +26,9 @@ namespace h3 {
 
 namespace {
 
-constexpr int kMaxTiles = 2048;  // key tiles per head (LDS bound)
+constexpr int kMaxTiles = 2048;            // key tiles per head (64 lanes x 32 scores)
 constexpr int kMaxSel = 1024;
+constexpr int kQT = 8;                     // query tiles (waves) per workgroup
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -32,114 +37,145 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void k_route(RouteArgs a) {
-  __shared__ float sS[4][kMaxTiles];
-  __shared__ int sSel[4][kMaxSel];
-  __shared__ float sQ[4][D];
-  __shared__ uint8_t sTaken[4][kMaxTiles];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= a.nh * a.nQ) return;  // whole wave exits together; no block barrier below
-  const int h = item / a.nQ, i = item % a.nQ;
+// PL: scores held per lane (tiles <= 64 PL)
+template <int D, int PL>
+__global__ __launch_bounds__(64 * kQT) void k_route(RouteArgs a) {
+  constexpr int SR = D + 4;  // LDS row stride (floats): 16-byte row reads of 16 lanes hit distinct banks
+  __shared__ __attribute__((aligned(16))) float sRow[64 * SR];
+  __shared__ __attribute__((aligned(16))) float sQ[kQT][D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, i = blockIdx.x * kQT + wave;
   const int nT = a.nT, npt = a.npt, nQ = a.nQ;
+  const bool active = i < nQ;  // an idle wave still takes part in the staging and barriers
+  const int ntl = (nT + 63) >> 6;
 
-  const float* qb = a.qbar + ((size_t)h * nQ + i) * D;
-  for (int c = lane; c < D; c += 64) sQ[wave][c] = qb[c];
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (active)
+    for (int c = lane; c < D; c += 64) sQ[wave][c] = a.qbar[((size_t)h * nQ + i) * D + c];
 
-  // ---- scores: lane per key tile, fp32 dot product in ascending c ----
-  const float scale = rsqrtf((float)D);
-  float* S = sS[wave];
-  bool any_nan = false;
-  for (int j = lane; j < nT; j += 64) {
-    const f32x4_t* kb = reinterpret_cast<const f32x4_t*>(a.kbar + ((size_t)h * nT + j) * D);
-    float s = 0.f;
-#pragma unroll 8
-    for (int c4 = 0; c4 < D / 4; ++c4) {
-      const f32x4_t kv = kb[c4];
-      s = fmaf(sQ[wave][4 * c4 + 0], kv[0], s);
-      s = fmaf(sQ[wave][4 * c4 + 1], kv[1], s);
-      s = fmaf(sQ[wave][4 * c4 + 2], kv[2], s);
-      s = fmaf(sQ[wave][4 * c4 + 3], kv[3], s);
+  // rows j0 .. j0+63 (those < nT) of a [nT][D] table into sRow
+  auto stage = [&](const float* src, int j0) {
+    const int rows = min(64, nT - j0);
+    for (int idx = tid; idx < 64 * (D / 4); idx += 64 * kQT) {
+      const int r = idx / (D / 4), c4 = idx % (D / 4);
+      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+      if (r < rows) v = *reinterpret_cast<const f32x4_t*>(src + (size_t)(j0 + r) * D + 4 * c4);
+      *reinterpret_cast<f32x4_t*>(&sRow[r * SR + 4 * c4]) = v;
     }
-    s *= scale;
-    S[j] = s;
-    any_nan |= (s != s);
-    a.scores[((size_t)h * nQ + i) * nT + j] = s;
+  };
+
+  // ---- scores: lane l scores tile 64 t + l ----
+  const float scale = rsqrtf((float)D);
+  const float* kb = a.kbar + (size_t)h * nT * D;
+  float* srow_out = a.scores + ((size_t)h * nQ + i) * nT;
+  float sc[PL];
+  bool any_nan = false;
+#pragma unroll
+  for (int t = 0; t < PL; ++t) {
+    sc[t] = 0.f;
+    if (t < ntl) {
+      __syncthreads();
+      stage(kb, 64 * t);
+      __syncthreads();
+      const int j = 64 * t + lane;
+      if (active && j < nT) {
+        const float* kr = &sRow[lane * SR];
+        float s = 0.f;
+#pragma unroll 8
+        for (int c4 = 0; c4 < D / 4; ++c4) {
+          const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kr + 4 * c4);
+          const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(&sQ[wave][4 * c4]);
+          s = fmaf(qv[0], kv[0], s);
+          s = fmaf(qv[1], kv[1], s);
+          s = fmaf(qv[2], kv[2], s);
+          s = fmaf(qv[3], kv[3], s);
+        }
+        s *= scale;
+        sc[t] = s;
+        any_nan |= (s != s);
+        srow_out[j] = s;
+      }
+    }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
   // ---- top-k over the video key tiles [npt, nT) ----
-  int* sel_out = a.sel + ((size_t)h * nQ + i) * a.nsel;
-  if (a.top_k >= nQ) {
-    for (int j = lane; j < nQ; j += 64) sel_out[j] = npt + j;
-  } else {
-    int* sl = sSel[wave];
-    uint8_t* taken = sTaken[wave];
-    for (int j = lane; j < nT; j += 64) taken[j] = 0;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    for (int it = 0; it < a.top_k; ++it) {
-      uint64_t best = 0;
-      for (int j = npt + lane; j < nT; j += 64) {
-        if (taken[j]) continue;
-        const uint64_t key = ((uint64_t)order_key(S[j]) << 32) | (uint32_t)(~j);
-        best = key > best ? key : best;
+  if (active) {
+    int* sel_out = a.sel + ((size_t)h * nQ + i) * a.nsel;
+    if (a.top_k >= nQ) {
+      for (int j = lane; j < nQ; j += 64) sel_out[j] = npt + j;
+    } else {
+      uint64_t key[PL];
+#pragma unroll
+      for (int t = 0; t < PL; ++t) {
+        const int j = 64 * t + lane;
+        key[t] = (t < ntl && j >= npt && j < nT)
+                     ? (((uint64_t)order_key(sc[t]) << 32) | (uint32_t)(~j))
+                     : 0ull;  // below every real key
       }
-      best = wave_max_u64(best);
-      const int win = (int)(~(uint32_t)best);
-      if (lane == 0) {
-        sl[it] = win;
-        taken[win] = 1;
+      uint64_t T = 0;  // the top_k-th largest key, built from the top bit down
+      for (int b = 63; b >= 0; --b) {
+        const uint64_t cand = T | (1ull << b);
+        int cnt = 0;
+#pragma unroll
+        for (int t = 0; t < PL; ++t)
+          if (t < ntl) cnt += __popcll(__ballot(key[t] >= cand));
+        if (cnt >= a.top_k) T = cand;
       }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    }
-    // ascending order by counting
-    for (int it = lane; it < a.top_k; it += 64) {
-      const int j = sl[it];
-      int rank = 0;
-      for (int u = 0; u < a.top_k; ++u) rank += sl[u] < j;
-      sel_out[rank] = j;
+      int off = 0;
+#pragma unroll
+      for (int t = 0; t < PL; ++t) {
+        if (t < ntl) {
+          const bool mine = key[t] >= T;
+          const uint64_t msk = __ballot(mine);
+          if (mine) sel_out[off + __popcll(msk & ((1ull << lane) - 1ull))] = 64 * t + lane;
+          off += __popcll(msk);
+        }
+      }
     }
   }
 
   // ---- pooled branch over all key tiles ----
-  if (!a.use_pooled) return;
+  if (!a.use_pooled) return;  // uniform over the grid
   any_nan = __any(any_nan);
   float m = -INFINITY;
-  for (int j = lane; j < nT; j += 64) m = fmaxf(m, S[j]);
+#pragma unroll
+  for (int t = 0; t < PL; ++t)
+    if (t < ntl && 64 * t + lane < nT) m = fmaxf(m, sc[t]);
   m = wave_max(m);
   float l = 0.f;
-  for (int j = lane; j < nT; j += 64) {
-    const float w = __expf(S[j] - m);
-    S[j] = w;
-    l += w;
+#pragma unroll
+  for (int t = 0; t < PL; ++t) {
+    const bool ok = t < ntl && 64 * t + lane < nT;
+    sc[t] = ok ? __expf(sc[t] - m) : 0.f;
+    l += sc[t];
   }
   l = wave_sum(l);
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const float inv_l = 1.0f / l;
-  float* po = a.pooled + ((size_t)h * nQ + i) * D;
-  for (int c = lane; c < D; c += 64) {
-    float acc = 0.f;
-    const float* vb = a.vbar + (size_t)h * nT * D + c;
-    for (int j = 0; j < nT; ++j) acc = fmaf(S[j], vb[(size_t)j * D], acc);
-    po[c] = any_nan ? __uint_as_float(0x7fc00000u) : acc * inv_l;
+  const float* vb = a.vbar + (size_t)h * nT * D;
+  float acc[D / 64];
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
+#pragma unroll
+  for (int t = 0; t < PL; ++t) {
+    if (t < ntl) {
+      __syncthreads();
+      stage(vb, 64 * t);
+      __syncthreads();
+      // rows past nT are staged as zeros and their weights are 0: adding
+      // 0 * 0 leaves the sum unchanged, so all 64 rows run unconditionally
+#pragma unroll 16
+      for (int r = 0; r < 64; ++r) {
+        const float w = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc[t]), r));
+#pragma unroll
+        for (int u = 0; u < D / 64; ++u) acc[u] = fmaf(w, sRow[r * SR + lane + 64 * u], acc[u]);
+      }
+    }
+  }
+  if (active) {
+    const float inv_l = 1.0f / l;
+    float* po = a.pooled + ((size_t)h * nQ + i) * D;
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u)
+      po[lane + 64 * u] = any_nan ? __uint_as_float(0x7fc00000u) : acc[u] * inv_l;
   }
 }
 
@@ -147,11 +183,19 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
 
 bool route_shape_ok(int nT, int top_k) { return nT <= kMaxTiles && top_k <= kMaxSel; }
 
+template <int D>
+static void launch_d(int ntl, dim3 grid, dim3 block, const RouteArgs& a, hipStream_t s) {
+  if (ntl <= 4) hipLaunchKernelGGL((k_route<D, 4>), grid, block, 0, s, a);
+  else if (ntl <= 8) hipLaunchKernelGGL((k_route<D, 8>), grid, block, 0, s, a);
+  else if (ntl <= 16) hipLaunchKernelGGL((k_route<D, 16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_route<D, 32>), grid, block, 0, s, a);
+}
+
 hipError_t launch_route(int head_dim, const RouteArgs& a, hipStream_t s) {
-  const int items = a.nh * a.nQ;
-  dim3 grid((items + 3) / 4), block(256);
-  if (head_dim == 128) hipLaunchKernelGGL(k_route<128>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_route<64>, grid, block, 0, s, a);
+  dim3 grid((a.nQ + kQT - 1) / kQT, a.nh), block(64 * kQT);
+  const int ntl = (a.nT + 63) / 64;
+  if (head_dim == 128) launch_d<128>(ntl, grid, block, a, s);
+  else launch_d<64>(ntl, grid, block, a, s);
   return hipGetLastError();
 }
 
