@@ -6,18 +6,20 @@
 // (QKV rows interleaved per attention head, consumed directly by the fused
 // Q/K norm + RoPE kernel).
 //
-// One workgroup per (tile, head).  The tile's rows are processed 32 padded
-// rows at a time (4 waves x 8 rows).  For a row, lanes 0-31 handle q and
-// lanes 32-63 handle k; each lane owns D/64 rotary pairs (i, i + D/2):
+// One workgroup (4 waves) per (head, tile); heads vary fastest over the grid
+// so the 40 workgroups of a tile share its rows of y and of the rotary table
+// in L2.  The tile is processed 32 padded rows at a time.  A q or k row is
+// D/8 lanes x 16 bytes (8 elements per lane), so a wave handles 64/(D/8) row
+// vectors at once:
 //   u~ = bf( rope( u * (sum u^2 / D + eps)^-1/2 * gain ) )
-//   rope: (a, b) -> (a cos - b sin, b cos + a sin),  cos/sin from the caller's table
-// v is copied unchanged and written transposed (v^T [nh][D][Rp]) through LDS, so
-// that the attention kernel reads runs of keys per head dimension; within each
-// aligned 16-row group the middle two 4-row blocks are swapped (see below).
-// Padded rows (beyond a tile's length, up to the next multiple of 32) are
-// written as zeros.  Tile sums of q~, k~ and v are kept in fp32 per lane, then
-// combined across the waves in a fixed order and divided by the tile's true
-// row count.
+//   rope: (a, b) -> (a cos - b sin, b cos + a sin) on the pairs (i, i + D/2),
+//   cos/sin from the caller's table; the partner element sits D/16 lanes away.
+// v rows are staged in LDS and written transposed (v^T [nh][D][Rp]) in
+// 16-byte runs of 8 positions; within each aligned 16-row group the middle
+// two 4-row blocks are swapped (see below).  Padded rows (beyond a tile's
+// length, up to the next multiple of 32) are written as zeros.  Tile sums of
+// q~, k~ and v are kept in fp32 per lane, combined across lanes and waves in
+// a fixed order, and divided by the tile's true row count.
 #include "common.h"
 #include "internal.h"
 
@@ -27,144 +29,174 @@ namespace {
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
-  constexpr int PPL = D / 64;       // rotary pairs per lane (32 lanes per q or k row)
-  constexpr int VPL = D / 64;       // v elements per lane (64 lanes per v row)
-  constexpr int SV = D + 2;         // LDS row stride (bf16) of the v staging tile
-  __shared__ bf16_t sV[32 * SV];
+  constexpr int LPR = D / 8;        // lanes per row vector (16 bytes each)
+  constexpr int RPW = 64 / LPR;     // row vectors per wave per iteration
+  constexpr int NIT = 64 / (4 * RPW);  // iterations for the 32 q + 32 k rows of a group
+  constexpr int SV = D + 8;         // LDS row stride (bf16) of the v staging tile
+  __shared__ __attribute__((aligned(16))) bf16_t sV[32 * SV];
   __shared__ float sSum[4][3][D];
 
-  const int t = blockIdx.x, h = blockIdx.y;
+  const int h = blockIdx.x, t = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r_beg = a.tstart[t], len = a.tstart[t + 1] - r_beg;
   const int ps = a.tpstart[t], plen = a.tpstart[t + 1] - ps;
-  const int hl = lane & 31;         // lane within the q (or k) half-wave
-  const bool is_k = lane >= 32;
+  const int u = lane % LPR, slot = lane / LPR;  // 16-byte unit within the row, row slot
+  const bool hi_half = u >= LPR / 2;            // holds elements i + D/2 of the rotary pairs
 
-  const float* gainp = nullptr;
-  float gain[2 * PPL];
+  float g8[2][8];  // q and k gains of this lane's 8 columns
   if constexpr (MODE == HEADS_QKV) {
-    const bf16_t* g = is_k ? a.k_gain : a.q_gain;
 #pragma unroll
-    for (int p = 0; p < PPL; ++p) {
-      gain[p] = bf2f(g[PPL * hl + p]);
-      gain[PPL + p] = bf2f(g[D / 2 + PPL * hl + p]);
+    for (int e = 0; e < 8; ++e) {
+      g8[0][e] = bf2f(a.q_gain[8 * u + e]);
+      g8[1][e] = bf2f(a.k_gain[8 * u + e]);
     }
   }
-  (void)gainp;
-
-  float qk_sum[2 * PPL];
-  float v_sum[VPL];
+  float sum[3][8];  // q, k, v column sums of this lane (columns 8u .. 8u+7)
 #pragma unroll
-  for (int p = 0; p < 2 * PPL; ++p) qk_sum[p] = 0.f;
+  for (int w = 0; w < 3; ++w)
 #pragma unroll
-  for (int p = 0; p < VPL; ++p) v_sum[p] = 0.f;
+    for (int e = 0; e < 8; ++e) sum[w][e] = 0.f;
 
-  bf16_t* qk_out = is_k ? a.k : a.q;
+  auto src_of = [&](int which, int row) -> const bf16_t* {
+    if constexpr (MODE == HEADS_QKV)
+      return a.y + (size_t)row * (3 * a.H) + h * 3 * D + which * D + 8 * u;
+    else
+      return (which == 0 ? a.q_in : which == 1 ? a.k_in : a.v_in) + ((size_t)h * a.R + row) * D +
+             8 * u;
+  };
   const float inv_d = 1.0f / (float)D;
 
   for (int c0 = 0; c0 < plen; c0 += 32) {
-    for (int j = 0; j < 8; ++j) {
-      const int rl = c0 + wave * 8 + j;       // row within the padded tile
+    // ---- q / k: row vector v = (it * 4 + wave) * RPW + slot; v < 32 is q ----
+    u32x4_t raw[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int v = (it * 4 + wave) * RPW + slot;
+      const int rl = c0 + (v & 31);
+      raw[it] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (rl < len) raw[it] = *reinterpret_cast<const u32x4_t*>(src_of(v >> 5, r_beg + rl));
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int v = (it * 4 + wave) * RPW + slot;
+      constexpr int kStride = 4 * RPW;             // row vectors per iteration (all waves)
+      const int which = (it * kStride) >> 5;       // = v >> 5, known at compile time
+      const int rl = c0 + (v & 31);
       const bool real = rl < len;
-      const int row = r_beg + rl;
-      // ---- q / k ----
-      float lo[PPL], hi[PPL];
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bflo(raw[it][e]);
+        x[2 * e + 1] = bfhi(raw[it][e]);
+      }
+      if constexpr (MODE == HEADS_QKV) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) ss += __shfl_xor(ss, o, kWave);
+        const float rinv = rsqrtf(ss * inv_d + a.eps);
+        const float* gg = g8[which];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = x[e] * rinv * gg[e];
+        if (a.rope) {
+          // cos/sin of pairs i = 8 (u mod LPR/2) + e of this row
+          const float* cs = a.rope + ((size_t)(r_beg + (real ? rl : 0)) * (D / 2) +
+                                      8 * (u % (LPR / 2))) * 2;
+          f32x4_t c4[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) c4[q4] = *reinterpret_cast<const f32x4_t*>(cs + 4 * q4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float c = c4[e >> 1][(e & 1) * 2], sn = c4[e >> 1][(e & 1) * 2 + 1];
+            const float other = __shfl_xor(x[e], LPR / 2, kWave);
+            // lo lane: a = x, b = other -> a c - b s; hi lane: b = x, a = other -> b c + a s
+            x[e] = hi_half ? fmaf(x[e], c, other * sn) : fmaf(x[e], c, -(other * sn));
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = bf2f(f2bf(x[e]));
+      }
+      u32x4_t w = {0u, 0u, 0u, 0u};
       if (real) {
-        const bf16_t* src;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[which][e] += x[e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack2(x[2 * e], x[2 * e + 1]);
+      }
+      bf16_t* dst = (which == 0 ? a.q : a.k) + ((size_t)h * a.Rp + ps + rl) * D + 8 * u;
+      *reinterpret_cast<u32x4_t*>(dst) = w;
+    }
+    // ---- v: 32 rows x LPR units, staged row-major in LDS ----
+#pragma unroll
+    for (int k2 = 0; k2 < 32 * LPR / 256; ++k2) {
+      const int unit = k2 * 256 + tid;
+      const int r = unit / LPR, uu = unit % LPR;
+      const int rl = c0 + r;
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (rl < len) {
         if constexpr (MODE == HEADS_QKV)
-          src = a.y + (size_t)row * (3 * a.H) + h * 3 * D + (is_k ? D : 0);
+          w = *reinterpret_cast<const u32x4_t*>(a.y + (size_t)(r_beg + rl) * (3 * a.H) +
+                                                 h * 3 * D + 2 * D + 8 * uu);
         else
-          src = (is_k ? a.k_in : a.q_in) + ((size_t)h * a.R + row) * D;
-#pragma unroll
-        for (int p = 0; p < PPL; ++p) {
-          lo[p] = bf2f(src[PPL * hl + p]);
-          hi[p] = bf2f(src[D / 2 + PPL * hl + p]);
-        }
-        if constexpr (MODE == HEADS_QKV) {
-          float ss = 0.f;
-#pragma unroll
-          for (int p = 0; p < PPL; ++p) {
-            ss = fmaf(lo[p], lo[p], ss);
-            ss = fmaf(hi[p], hi[p], ss);
-          }
-          ss = half_sum(ss);
-          const float rinv = rsqrtf(ss * inv_d + a.eps);
-#pragma unroll
-          for (int p = 0; p < PPL; ++p) {
-            const float x0 = lo[p] * rinv * gain[p];
-            const float x1 = hi[p] * rinv * gain[PPL + p];
-            if (a.rope) {
-              const float* cs = a.rope + ((size_t)row * (D / 2) + PPL * hl + p) * 2;
-              const float c = cs[0], s = cs[1];
-              lo[p] = bf2f(f2bf(x0 * c - x1 * s));
-              hi[p] = bf2f(f2bf(x1 * c + x0 * s));
-            } else {
-              lo[p] = bf2f(f2bf(x0));
-              hi[p] = bf2f(f2bf(x1));
-            }
-          }
-        }
-#pragma unroll
-        for (int p = 0; p < PPL; ++p) {
-          qk_sum[p] += lo[p];
-          qk_sum[PPL + p] += hi[p];
-        }
-      } else {
-#pragma unroll
-        for (int p = 0; p < PPL; ++p) lo[p] = hi[p] = 0.f;
+          w = *reinterpret_cast<const u32x4_t*>(a.v_in + ((size_t)h * a.R + r_beg + rl) * D +
+                                                 8 * uu);
       }
-      bf16_t* dst = qk_out + ((size_t)h * a.Rp + ps + rl) * D;
-#pragma unroll
-      for (int p = 0; p < PPL; ++p) {
-        dst[PPL * hl + p] = f2bf(lo[p]);
-        dst[D / 2 + PPL * hl + p] = f2bf(hi[p]);
-      }
-      // ---- v (all 64 lanes) ----
-      const int rr = wave * 8 + j;
-#pragma unroll
-      for (int p = 0; p < VPL; ++p) {
-        bf16_t vb = 0;
-        if (real) {
-          if constexpr (MODE == HEADS_QKV)
-            vb = a.y[(size_t)row * (3 * a.H) + h * 3 * D + 2 * D + VPL * lane + p];
-          else
-            vb = a.v_in[((size_t)h * a.R + row) * D + VPL * lane + p];
-          v_sum[p] += bf2f(vb);
-        }
-        sV[rr * SV + VPL * lane + p] = vb;
-      }
+      *reinterpret_cast<u32x4_t*>(&sV[r * SV + 8 * uu]) = w;
     }
     __syncthreads();
-    // v^T: thread -> (dimension c, 4 consecutive rows).  Within every aligned
-    // group of 16 rows the 4-row blocks are stored in the order 0, 2, 1, 3, so
-    // that the 8 keys one lane feeds to the value-product MFMA (rows 4g..4g+3
-    // and 8+4g..8+4g+3 of a 16-row group) are 16 contiguous bytes.
-    for (int idx = tid; idx < D * 8; idx += 256) {
-      const int c = idx >> 3, r4 = (idx & 7) * 4;
-      u32x2_t w;
-      w[0] = (uint32_t)sV[(r4 + 0) * SV + c] | ((uint32_t)sV[(r4 + 1) * SV + c] << 16);
-      w[1] = (uint32_t)sV[(r4 + 2) * SV + c] | ((uint32_t)sV[(r4 + 3) * SV + c] << 16);
-      const int blk = (r4 >> 2) & 3;
-      const int pos = (r4 & ~12) | (((blk == 1) ? 2 : (blk == 2) ? 1 : blk) << 2);
-      *reinterpret_cast<u32x2_t*>(a.vt + ((size_t)h * D + c) * a.Rp + ps + c0 + pos) = w;
+    // v sums: this lane's columns 8u..8u+7 over rows slot, slot + RPW, ... of the
+    // wave's share (rows wave * 8 .. wave * 8 + 7)
+    for (int r = wave * 8 + slot; r < wave * 8 + 8; r += RPW) {
+      if (c0 + r < len) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&sV[r * SV + 8 * u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum[2][2 * e] += bflo(w[e]);
+          sum[2][2 * e + 1] += bfhi(w[e]);
+        }
+      }
+    }
+    // v^T: thread -> (dimension d, 8 positions).  Within every aligned group of
+    // 16 rows the 4-row blocks are stored in the order 0, 2, 1, 3, so that the
+    // 8 keys one lane feeds to the value-product MFMA (rows 4g..4g+3 and
+    // 8+4g..8+4g+3 of a 16-row group) are 16 contiguous bytes: positions
+    // 8h8 .. 8h8+7 of a group hold rows 4h8..4h8+3 and 8+4h8..8+4h8+3.
+#pragma unroll
+    for (int k2 = 0; k2 < D * 4 / 256; ++k2) {
+      const int idx = k2 * 256 + tid;
+      const int d = idx % D, p8 = idx / D;  // p8: 8-position run 0..3 of the 32-row group
+      const int g16 = p8 >> 1, h8 = p8 & 1;
+      const int r0 = 16 * g16 + 4 * h8, r1 = r0 + 8;
+      u32x4_t w;
+      w[0] = (uint32_t)sV[(r0 + 0) * SV + d] | ((uint32_t)sV[(r0 + 1) * SV + d] << 16);
+      w[1] = (uint32_t)sV[(r0 + 2) * SV + d] | ((uint32_t)sV[(r0 + 3) * SV + d] << 16);
+      w[2] = (uint32_t)sV[(r1 + 0) * SV + d] | ((uint32_t)sV[(r1 + 1) * SV + d] << 16);
+      w[3] = (uint32_t)sV[(r1 + 2) * SV + d] | ((uint32_t)sV[(r1 + 3) * SV + d] << 16);
+      *reinterpret_cast<u32x4_t*>(a.vt + ((size_t)h * D + d) * a.Rp + ps + c0 + 8 * p8) = w;
     }
     __syncthreads();
   }
 
-  // ---- tile means ----
+  // ---- tile means: lanes with the same columns (slots), then waves, fixed order ----
 #pragma unroll
-  for (int p = 0; p < PPL; ++p) {
-    sSum[wave][is_k ? 1 : 0][PPL * hl + p] = qk_sum[p];
-    sSum[wave][is_k ? 1 : 0][D / 2 + PPL * hl + p] = qk_sum[PPL + p];
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) sum[w][e] += __shfl_xor(sum[w][e], o, kWave);
+  if (slot == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sSum[wave][w][8 * u + e] = sum[w][e];
   }
-#pragma unroll
-  for (int p = 0; p < VPL; ++p) sSum[wave][2][VPL * lane + p] = v_sum[p];
   __syncthreads();
   const float inv_len = 1.0f / (float)len;
   for (int idx = tid; idx < 3 * D; idx += 256) {
     const int which = idx / D, c = idx % D;
-    const float s = ((sSum[0][which][c] + sSum[1][which][c]) + sSum[2][which][c]) + sSum[3][which][c];
-    const float m = s * inv_len;
+    const float sm = ((sSum[0][which][c] + sSum[1][which][c]) + sSum[2][which][c]) + sSum[3][which][c];
+    const float m = sm * inv_len;
     if (which == 0) {
       if (t >= a.npt) a.qbar[((size_t)h * (a.nT - a.npt) + (t - a.npt)) * D + c] = m;
     } else if (which == 1) {
@@ -178,7 +210,7 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
 }  // namespace
 
 hipError_t launch_heads(int mode, int head_dim, const HeadsArgs& a, hipStream_t s) {
-  dim3 grid(a.nT, a.nh), block(256);
+  dim3 grid(a.nh, a.nT), block(256);
   if (head_dim == 128) {
     if (mode == HEADS_QKV) hipLaunchKernelGGL((k_heads<128, HEADS_QKV>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_heads<128, HEADS_SPLIT>), grid, block, 0, s, a);
