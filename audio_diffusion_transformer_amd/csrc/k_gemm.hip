@@ -16,17 +16,20 @@
 // swizzled by (row / 2) % 8, which makes the fragment reads (16 consecutive
 // rows, same chunk) hit 16 distinct bank groups.
 //
-// Schedule (ping-pong): waves w and w + 4 share a SIMD.  Waves 0-3 and 4-7
-// run the same sequence of phases one phase apart, so that while one wave of
-// a SIMD runs its MFMA phase (16 products, half a stage) the other issues its
-// memory phase (fragment reads for its next MFMA phase and, once per stage,
-// its share of the next stage's loads).  All eight waves meet at a barrier
-// between phases.  The loads of stage s+1 go into the buffer that stage s-1
-// used; they are issued in the first memory phase of stage s and waited for
-// before the barrier that precedes the first read of stage s+1.  The loads
-// are issued as inline assembly (scalar base address, per-lane 32-bit
-// offsets) so that the compiler does not insert its own conservative waits
-// for them; this kernel waits on vmcnt itself.
+// Schedule (ping-pong): waves w and w + 4 share a SIMD.  Waves 0-3 (group 0)
+// and 4-7 (group 1) run the same sequence of phases one phase apart: in its
+// memory phase a wave reads the fragments of a whole stage (24 LDS reads), in
+// its MFMA phase it issues the stage's 32 products; while one wave of a SIMD
+// computes, the other reads.  All eight waves meet at a barrier between
+// phases.  Each group loads half of every stage: group 0 issues its half of
+// stage s+1 at the start of its memory phase of stage s (the buffer's last
+// readers finished a phase earlier); group 1 issues its half of stage s+2 at
+// the end of its memory phase of stage s, right after its own reads of that
+// buffer.  Both thus have two phases to land their loads before the barrier
+// that precedes the first read.  The loads are issued as inline assembly
+// (scalar base address, per-lane 32-bit offsets) so that the compiler does
+// not insert its own conservative waits for them; this kernel waits on vmcnt
+// itself.
 //
 // Workgroup ids are remapped so that each XCD (ids are dealt round-robin over
 // the 8 XCDs) works on a contiguous band of tiles; within a band tiles are
@@ -161,15 +164,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // fragments of half a stage (k-steps 2 hs, 2 hs + 1): A rows wm*128 + 32i + l%32,
+  // fragments of a stage (k-steps kk = 0..3): A rows wm*128 + 32i + l%32,
   // B rows wn*64 + 32j + l%32, k = 16 kk + 8 (l / 32) .. + 7
-  bf16x8_t fa[2][4], fb[2][2];
-  auto read_frags = [&](int s, int hs) {
+  bf16x8_t fa[4][4], fb[4][2];
+  auto read_frags = [&](int s) {
     const bf16_t* sa = smem + (s & 1) * 2 * STAGE;
     const bf16_t* sb = sa + STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int gc = (hs * 2 + kk) * 2 + half;
+    for (int kk = 0; kk < 4; ++kk) {
+      const int gc = kk * 2 + half;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wm * 128 + i * 32 + lr;
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
   };
   auto products = [&]() {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -194,23 +197,32 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
 
   const int KT = K / BK;  // >= 2
   issue(0);
-  __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+  if (grp == 1) {
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(H3_VMCNT(8));  // stage 0 landed; stage 1 may be in flight
+  } else {
+    __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+  }
   phase_barrier();
   if (grp == 1) phase_barrier();  // the second group runs one phase behind
   for (int s = 0; s < KT; ++s) {
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-      // memory phase
-      if (hs == 0 && s + 1 < KT) issue(s + 1);
-      read_frags(s, hs);
-      __builtin_amdgcn_s_waitcnt(H3_LGKMCNT0);
-      if (grp == 1 && hs == 1 && s + 1 < KT) __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
-      phase_barrier();
-      // MFMA phase
-      products();
-      if (grp == 0 && hs == 1 && s + 1 < KT) __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
-      phase_barrier();
+    // memory phase
+    if (grp == 0 && s + 1 < KT) issue(s + 1);
+    read_frags(s);
+    __builtin_amdgcn_s_waitcnt(H3_LGKMCNT0);
+    if (grp == 1) {
+      if (s + 2 < KT) {
+        issue(s + 2);
+        __builtin_amdgcn_s_waitcnt(H3_VMCNT(8));  // this wave's half of stage s+1 has landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+      }
     }
+    phase_barrier();
+    // MFMA phase
+    products();
+    if (grp == 0 && s + 1 < KT) __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+    phase_barrier();
   }
   if (grp == 0) phase_barrier();
   __builtin_amdgcn_s_waitcnt(0);
