@@ -39,7 +39,54 @@ def parse():
     ap.add_argument("--blocks", type=int, default=N_BLOCKS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prof", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) three "
+                         "times, to scale the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE) of this script, each scaled by what the same
+# counter reads for the plain copy of --copy-calibration (profiles/
+# gemm_fc1_hbm_traffic.md has the commands and raw values).  Valid only for the
+# kernel sources it was measured on: when their sha256 differs, the traffic is
+# reported as null.
+TRAFFIC = {
+    "kernel": "gemm_fc1",
+    "sources": ["audio_diffusion_transformer_amd/csrc/k_gemm.hip",
+                "audio_diffusion_transformer_amd/csrc/common.h",
+                "audio_diffusion_transformer_amd/csrc/internal.h"],
+    "sources_sha256": "b9e1debff0f81bf711672e4760dbfe2cd0d4ea88d3a884b93fe394c37157ca87",
+    # raw KiB per dispatch and the copy's scale factors (1 GiB copy: FETCH_SIZE
+    # 524294.5 KiB, WRITE_SIZE 1048576.0 KiB)
+    "fetch_kib": 2563252.5, "fetch_scale": 1.999975,
+    "write_kib": 617400.0, "write_scale": 1.000000,
+}
+
+
+def measured_traffic(kernel):
+    if TRAFFIC is None or TRAFFIC["kernel"] != kernel:
+        return None
+    import hashlib
+    h = hashlib.sha256()
+    for src in TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != TRAFFIC["sources_sha256"]:
+        return None
+    return round(TRAFFIC["fetch_kib"] * 1024 * TRAFFIC["fetch_scale"] +
+                 TRAFFIC["write_kib"] * 1024 * TRAFFIC["write_scale"])
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28                      # 2^28 fp32 = 1 GiB each way
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)      # one elementwise kernel: reads 1 GiB, writes 1 GiB
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
 def kernel_work(sh, ts, npt, plan_sel_rows):
@@ -113,6 +160,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
               f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     from audio_diffusion_transformer_amd import binding as B
@@ -194,11 +245,11 @@ def main():
         if kind == "mfma":
             roofline = {"bound": "mfma", "kernel": dom, "achieved": e["achieved_tflops"],
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": e["frac"],
-                        "traffic": None}
+                        "traffic": measured_traffic(dom)}
         else:
             roofline = {"bound": "hbm", "kernel": dom, "achieved": e["achieved_gbs"],
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": e["frac"],
-                        "traffic": None}
+                        "traffic": measured_traffic(dom)}
         gemm_flop = sum(work[k][1] * kernels[k]["launches"] for k in kernels
                         if k.startswith("gemm_"))
         gemm_ms = sum(kernels[k]["total_ms"] for k in kernels if k.startswith("gemm_"))
