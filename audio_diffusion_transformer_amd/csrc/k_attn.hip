@@ -118,6 +118,7 @@ void k_attn(AttnArgs a) {
   }
   const int4 qb = a.qblocks[qbi];
   const int tile = qb.x, prow0 = qb.y, nrows = qb.z, row0 = qb.w;
+  const bool q_live = qh * 32 < nrows;  // this wave's query half holds real rows
   const bool dense = tile < a.npt;
 
   for (int c = tid; c < a.n_chunks; c += 256) sValid[c] = (uint8_t)a.chunk_valid[c];
@@ -247,7 +248,9 @@ void k_attn(AttnArgs a) {
       chunk = chunk_at(ci + 2);
       issue(cur ^ 1, chunk);
     }
-    if (ci >= nchunk) continue;
+    // past the end of this stream's list, or no real query in this half (a
+    // block of at most 32 rows): only the loads and barriers above
+    if (ci >= nchunk || !q_live) continue;
     const int valid = sValid[this_chunk];
     const bf16_t* kb = sbuf + cur * STG;
     const bf16_t* vb = kb + CH;

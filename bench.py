@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--blocks", type=int, default=N_BLOCKS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prof", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--attn-sweep", action="store_true",
+                    help="only time h3_routed_attn at 15,435 rows x 40 heads x 128 over tile "
+                         "size {32, 64, 128} x top-k {8, 32, all}; one JSON line per case")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) three "
                          "times, to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -76,6 +79,68 @@ def measured_traffic(kernel):
         return None
     return round(TRAFFIC["fetch_kib"] * 1024 * TRAFFIC["fetch_scale"] +
                  TRAFFIC["write_kib"] * 1024 * TRAFFIC["write_scale"])
+
+
+def attn_sweep():
+    """Routed-attention workload: q, k, v ~ bf16 N(0, 1) [40][15,435][128] with the
+    seeded rank-4 field on the video rows of q and k.  Algorithmic FLOP per
+    call = 4 d nh sum over query rows of the keys they attend, counted exactly
+    from the returned selection (dense rows: all R; video rows: the prefix and
+    the rows of the selected tiles).  Times are HIP events around the kernel
+    launches (h3_prof), median of 5 calls after 2 warm-up calls."""
+    import torch
+    from audio_diffusion_transformer_amd import binding as B
+    from audio_diffusion_transformer_amd import synth as S
+    from audio_diffusion_transformer_amd import tensors as T
+    base = S.FULL
+    q, k, v = S.attn_qkv(base)   # the field depends on the video row index only
+    qd, kd, vd = T.to_dev(q), T.to_dev(k), T.to_dev(v)
+    del q, k, v
+    for ts_size in (32, 64, 128):
+        sh0 = S.Shape(base.n_text, base.n_audio, base.n_video, base.hidden, base.n_heads,
+                      base.head_dim, base.ffn, tile=ts_size, top_k=1, pooled=1)
+        for top_k in (8, 32, 0):
+            ts, npt = S.tile_map(sh0)
+            nq = len(ts) - 1 - npt
+            kk = nq if top_k == 0 else top_k
+            sh = S.Shape(base.n_text, base.n_audio, base.n_video, base.hidden, base.n_heads,
+                         base.head_dim, base.ffn, tile=ts_size, top_k=kk, pooled=1)
+            shape = B.make_shape(sh, ts, npt)
+            lay = B.workspace_layout(shape, ts, B.H3_WS_ATTN)
+            ws = T.workspace(lay.total)
+            nh, R, d = sh.n_heads, sh.rows, sh.head_dim
+            out = T.bf16_empty((R, nh * d))
+            sel = torch.empty((nh, max(nq, 1), max(lay.n_sel, 1)), dtype=torch.int32,
+                              device="cuda")
+            for _ in range(2):
+                B.routed_attn(shape, ts, qd, kd, vd, out, ws, sel=sel)
+            torch.cuda.synchronize()
+            times = {}
+            for _ in range(5):
+                B.prof_enable(True)
+                B.routed_attn(shape, ts, qd, kd, vd, out, ws, sel=sel)
+                torch.cuda.synchronize()
+                for name, (n, ms) in B.prof_read().items():
+                    if n:
+                        times.setdefault(name, []).append(ms)
+                B.prof_enable(False)
+            lens = np.diff(np.asarray(ts, np.int64))
+            P = sh.n_prefix
+            sel_h = sel.cpu().numpy()[:, :nq, :lay.n_sel]
+            vid_len = lens[npt:]
+            q_rows = vid_len[np.arange(nq)]                   # rows of each video query tile
+            sel_rows = lens[sel_h].sum(axis=2)                # [nh][nq] keys from the selected tiles
+            keys = nh * P * R + float(((P + sel_rows) * q_rows[None, :]).sum())
+            flop = 4.0 * d * keys
+            med = {n: float(np.median(t)) for n, t in times.items()}
+            ach = flop / (med["attn"] * 1e-3) / 1e12
+            print(json.dumps({"tile": ts_size, "top_k": "all" if top_k == 0 else top_k,
+                              "video_query_tiles": nq, "attn_ms": round(med["attn"], 4),
+                              "heads_ms": round(med.get("heads", 0.0), 4),
+                              "route_ms": round(med.get("route", 0.0), 4),
+                              "attn_flop": flop, "attn_tflops": round(ach, 1),
+                              "attn_frac_of_2500": round(ach / PEAK_BF16_TFLOPS, 4)}),
+                  flush=True)
 
 
 def copy_calibration():
@@ -163,6 +228,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.attn_sweep:
+        attn_sweep()
         return
 
     import torch
