@@ -4,12 +4,12 @@
 // q/k/v products, out projection, MLP in / out; "Precision": bf16 operands,
 // fp32 sums).  Both operands are K-contiguous ([row][K] activations, [out][in]
 // weights), which is the per-lane operand order of the CDNA4 MFMA:
-// v_mfma_f32_32x32x16_bf16 takes 8 consecutive K elements of one A row and of
+// v_mfma_f32_16x16x32_bf16 takes 8 consecutive K elements of one A row and of
 // one B row per lane.
 //
 // Tiling: a 512-thread workgroup (8 wave64, two per SIMD) owns a 256x256 C
-// tile; wave w owns the 128x64 sub-tile (w/4, w%4) as 4x2 MFMA blocks of 32x32
-// (128 fp32 accumulators per lane).  K advances 64 at a time through a
+// tile; wave w owns the 128x64 sub-tile (w/4, w%4) as 8x4 blocks of 16x16
+// computed with v_mfma_f32_16x16x32_bf16 (128 fp32 accumulators per lane).  K advances 64 at a time through a
 // two-stage LDS ring filled by global_load_lds_dwordx4: each lane's 16 bytes
 // go straight to LDS, so no registers hold staged tiles.  A stage row is one
 // full 128-byte line of A or B; its eight 16-byte chunks are stored XOR-
@@ -155,44 +155,47 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
     }
   };
 
-  const int lr = lane & 31, half = lane >> 5;
-  f32x16_t acc[4][2];
+  // v_mfma_f32_16x16x32_bf16: lane l supplies row l%16 of a 16-row block and
+  // the 8 k-values 8 (l/16) .. +7 of a 32-wide k-step (A and B alike); the
+  // result block holds, in lane l, column l%16 and rows 4 (l/16) .. +3.
+  const int l16 = lane & 15, q4 = lane >> 4;
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
-  // fragments of a stage (k-steps kk = 0..3): A rows wm*128 + 32i + l%32,
-  // B rows wn*64 + 32j + l%32, k = 16 kk + 8 (l / 32) .. + 7
-  bf16x8_t fa[4][4], fb[4][2];
+  // fragments of a stage (k-steps kk = 0, 1 of 32): A rows wm*128 + 16i + l%16,
+  // B rows wn*64 + 16j + l%16, k-chunk 4 kk + l/16 (8 values each)
+  bf16x8_t fa[2][8], fb[2][4];
   auto read_frags = [&](int s) {
     const bf16_t* sa = smem + (s & 1) * 2 * STAGE;
     const bf16_t* sb = sa + STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int gc = kk * 2 + half;
+    for (int kk = 0; kk < 2; ++kk) {
+      const int gc = kk * 4 + q4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + i * 32 + lr;
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + i * 16 + l16;
         fa[kk][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + r * BK + (gc ^ swz(r)) * 8));
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + lr;
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 64 + j * 16 + l16;
         fb[kk][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + r * BK + (gc ^ swz(r)) * 8));
       }
     }
   };
   auto products = [&]() {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
   };
 
   const int KT = K / BK;  // >= 2
@@ -229,22 +232,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
   __syncthreads();
 
   // ---- epilogue ----
-  // Accumulator element e of block (i, j) in lane l sits at row 8(e/4) + 4(l/32)
-  // + e%4, column l%32 of that 32x32 block.  Each wave rounds its 128x64
-  // sub-tile into its own 16 KB of LDS, then writes it back in 16-byte chunks.
+  // Accumulator element e of block (i, j) in lane l sits at row 4(l/16) + e,
+  // column l%16 of that 16x16 block.  Each wave rounds its 128x64 sub-tile into
+  // its own 16 KB of LDS, then writes it back in 16-byte chunks.
   bf16_t* st = smem + wave * (128 * 64);
-  const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float bias = bf2f(ep.bias[n0 + wn * 64 + j * 32 + col_l]);
+  for (int j = 0; j < 4; ++j) {
+    const float bias = bf2f(ep.bias[n0 + wn * 64 + j * 16 + l16]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = i * 32 + 8 * (e >> 2) + row_l + (e & 3);
+      for (int e = 0; e < 4; ++e) {
+        const int r = i * 16 + 4 * q4 + e;
         float v = acc[i][j][e] + bias;
         if constexpr (EPI == EPI_BIAS_GELU) v = gelu_erf(v);
-        st[r * 64 + j * 32 + col_l] = f2bf(v);
+        st[r * 64 + j * 16 + l16] = f2bf(v);
       }
   }
   __builtin_amdgcn_s_waitcnt(0);
