@@ -119,10 +119,18 @@ class Shape:
     norm_eps: float = 1e-6
     c_video: int = 96
     c_audio: int = 32
+    mlp: int = 0            # 0: GELU MLP (F wide), 1: SwiGLU (FC1 2F wide, gate/up interleaved by 16 rows)
+    gate: int = 0           # 1: a fourth per-head product, the routing gate on the pooled branch
+    video_grid: tuple = ()  # (T, H, W) with cube > 0: video rows stored cube by cube
+    cube: int = 0           # edge of the cubic video tiles (0: runs of `tile` rows)
 
     @property
     def rows(self):
         return self.n_text + self.n_audio + self.n_video
+
+    @property
+    def attn_width(self):
+        return self.n_heads * self.head_dim
 
     @property
     def n_prefix(self):
@@ -138,31 +146,77 @@ MID = Shape(256, 256, 4096, 3072, 24, 128, 12288, tile=64, top_k=16)
 FULL = Shape(512, 543, 14380, 5120, 40, 128, 20480, tile=64, top_k=32)
 CONFIGS = {"tiny": TINY, "mid": MID, "full": FULL}
 
+# The pages' own FastH3 block and geometry: hidden 5,376, 56 heads x 128 (7,168),
+# SwiGLU 14,336, the routing gate; 36 text / 414 audio / 14,985 video rows, the
+# video a 37 x 15 x 27 grid cut into 4 x 4 x 4 cubes (280 video tiles, 8 prefix
+# tiles), top-k 56.  FASTH3_TINY keeps every feature at a size the oracle runs in
+# seconds (a 5 x 6 x 7 video grid, 3 x 3 x 3 cubes: 24 ragged video tiles).
+FASTH3 = Shape(36, 414, 14985, 5376, 56, 128, 14336, tile=64, top_k=56, mlp=1, gate=1,
+               video_grid=(37, 15, 27), cube=4)
+FASTH3_TINY = Shape(20, 50, 210, 256, 4, 64, 512, tile=64, top_k=6, mlp=1, gate=1,
+                    video_grid=(5, 6, 7), cube=3)
+
+
+def video_positions(shape: Shape):
+    """Raster index (t * H * W + h * W + w) of every video row.  With cubes the
+    rows are stored cube by cube (cubes in raster order of their corners, the
+    tokens of a cube in raster order), so that every cube is a contiguous run
+    of rows; otherwise the identity."""
+    if not shape.cube:
+        return np.arange(shape.n_video, dtype=np.int64)
+    T, Hh, W = shape.video_grid
+    assert T * Hh * W == shape.n_video, "video grid does not match the video row count"
+    c = shape.cube
+    out = []
+    for t0 in range(0, T, c):
+        for h0 in range(0, Hh, c):
+            for w0 in range(0, W, c):
+                t, h, w = np.meshgrid(np.arange(t0, min(t0 + c, T)), np.arange(h0, min(h0 + c, Hh)),
+                                      np.arange(w0, min(w0 + c, W)), indexing="ij")
+                out.append((t * Hh * W + h * W + w).reshape(-1))
+    return np.concatenate(out).astype(np.int64)
+
+
+def video_tile_sizes(shape: Shape):
+    """Row counts of the video tiles: runs of `tile` rows, or the cubes."""
+    if not shape.cube:
+        n = shape.n_video
+        return [min(shape.tile, n - s) for s in range(0, n, shape.tile)]
+    T, Hh, W = shape.video_grid
+    c = shape.cube
+    return [min(c, T - t0) * min(c, Hh - h0) * min(c, W - w0)
+            for t0 in range(0, T, c) for h0 in range(0, Hh, c) for w0 in range(0, W, c)]
+
 
 def tile_map(shape: Shape):
-    """Contiguous runs of ``shape.tile`` rows per segment, ragged last tile.
+    """Contiguous runs of ``shape.tile`` rows per prefix segment (ragged last
+    tile); video tiles are runs of ``shape.tile`` rows or, with cubes, the
+    cubes in storage order (see video_positions).
 
     Returns (tile_start int32 [n_tiles+1], n_prefix_tiles).
     """
     starts = []
     r = 0
     n_prefix_tiles = 0
-    for seg_i, n in enumerate((shape.n_text, shape.n_audio, shape.n_video)):
+    for n in (shape.n_text, shape.n_audio):
         for s in range(0, n, shape.tile):
             starts.append(r + s)
-            if seg_i < 2:
-                n_prefix_tiles += 1
+            n_prefix_tiles += 1
         r += n
+    for size in video_tile_sizes(shape):
+        starts.append(r)
+        r += size
     starts.append(r)
     return np.asarray(starts, dtype=np.int32), n_prefix_tiles
 
 
 def rope_tables(shape: Shape):
-    """fp32 [R][d/2][2] (cos, sin); position = row index within its segment,
-    angle_i = pos * 10000^(-2i/d)."""
+    """fp32 [R][d/2][2] (cos, sin); position = row index within its segment
+    (for video rows stored by cubes: the raster index), angle_i = pos *
+    10000^(-2i/d)."""
     d2 = shape.head_dim // 2
     pos = np.concatenate([np.arange(shape.n_text), np.arange(shape.n_audio),
-                          np.arange(shape.n_video)]).astype(np.float64)
+                          video_positions(shape)]).astype(np.float64)
     inv = 10000.0 ** (-2.0 * np.arange(d2, dtype=np.float64) / shape.head_dim)
     ang = pos[:, None] * inv[None, :]
     out = np.empty((shape.rows, d2, 2), dtype=np.float32)
@@ -171,21 +225,23 @@ def rope_tables(shape: Shape):
     return out
 
 
+def block_shapes(shape: Shape):
+    """Array shapes of one block's weights: QKV [(3 + gate) A][H] per head
+    [q|k|v(|g)], out projection [H][A], FC1 [F or 2F][H], FC2 [H][F]."""
+    H, F, d, A = shape.hidden, shape.ffn, shape.head_dim, shape.attn_width
+    nq = (4 if shape.gate else 3) * A
+    f1 = 2 * F if shape.mlp == 1 else F
+    return {"w_qkv": (nq, H), "b_qkv": (nq,), "q_gain": (d,), "k_gain": (d,),
+            "w_o": (H, A), "b_o": (H,), "w_fc1": (f1, H), "b_fc1": (f1,),
+            "w_fc2": (H, F), "b_fc2": (H,)}
+
+
 def block_weights(shape: Shape, block: int = 0, seed: int = SEED, std: float = 0.02):
-    H, F, d = shape.hidden, shape.ffn, shape.head_dim
     p = f"block{block}."
-    w = {
-        "w_qkv": normal_bf16(p + "w_qkv", (3 * H, H), std, seed=seed),
-        "b_qkv": normal_bf16(p + "b_qkv", (3 * H,), std, seed=seed),
-        "q_gain": normal_bf16(p + "q_gain", (d,), std, mean=1.0, seed=seed),
-        "k_gain": normal_bf16(p + "k_gain", (d,), std, mean=1.0, seed=seed),
-        "w_o": normal_bf16(p + "w_o", (H, H), std, seed=seed),
-        "b_o": normal_bf16(p + "b_o", (H,), std, seed=seed),
-        "w_fc1": normal_bf16(p + "w_fc1", (F, H), std, seed=seed),
-        "b_fc1": normal_bf16(p + "b_fc1", (F,), std, seed=seed),
-        "w_fc2": normal_bf16(p + "w_fc2", (H, F), std, seed=seed),
-        "b_fc2": normal_bf16(p + "b_fc2", (H,), std, seed=seed),
-    }
+    w = {}
+    for k, shp in block_shapes(shape).items():
+        mean = 1.0 if k in ("q_gain", "k_gain") else 0.0
+        w[k] = normal_bf16(p + k, shp, std, mean=mean, seed=seed)
     return w
 
 
@@ -226,7 +282,7 @@ def activations(shape: Shape, seed: int = SEED, field: bool = False, name="x_in"
     if not field:
         return x
     xf = bf16_bits_to_f32(x).astype(np.float64)
-    phi = lowrank_field(shape.n_video, 4, seed=seed, name=name + ".phi")
+    phi = lowrank_field(shape.n_video, 4, seed=seed, name=name + ".phi")[video_positions(shape)]
     basis = normal_f64(name + ".basis", (4, shape.hidden), seed=seed)
     xf[shape.n_prefix:] += phi @ basis
     return f32_to_bf16(xf.astype(np.float32))
@@ -241,7 +297,7 @@ def attn_qkv(shape: Shape, seed: int = SEED, correlated: bool = True, amp: float
     v = normal_bf16("attn.v", (nh, R, d), 1.0, seed=seed)
     if not correlated:
         return q, k, v
-    phi = lowrank_field(shape.n_video, 4, seed=seed, name="attn.phi")
+    phi = lowrank_field(shape.n_video, 4, seed=seed, name="attn.phi")[video_positions(shape)]
     A = normal_f64("attn.A", (nh, 4, d), seed=seed)
     B = normal_f64("attn.B", (nh, 4, d), seed=seed)
     P = shape.n_prefix
@@ -273,11 +329,9 @@ def device_normal_bf16(name, shape, std, seed=SEED, device="cuda", mean=0.0):
 
 def device_block_weights(shape: Shape, block: int = 0, seed: int = SEED, std: float = 0.02,
                          device="cuda"):
-    H, F, d = shape.hidden, shape.ffn, shape.head_dim
     p = f"block{block}."
-    sizes = {"w_qkv": (3 * H, H), "b_qkv": (3 * H,), "w_o": (H, H), "b_o": (H,),
-             "w_fc1": (F, H), "b_fc1": (F,), "w_fc2": (H, F), "b_fc2": (H,)}
-    w = {k: device_normal_bf16(p + k, s, std, seed, device) for k, s in sizes.items()}
-    for k in ("q_gain", "k_gain"):
-        w[k] = device_normal_bf16(p + k, (d,), std, seed, device, mean=1.0)
+    w = {}
+    for k, shp in block_shapes(shape).items():
+        mean = 1.0 if k in ("q_gain", "k_gain") else 0.0
+        w[k] = device_normal_bf16(p + k, shp, std, seed, device, mean=mean)
     return w

@@ -27,7 +27,9 @@ top-k.  Matrix products use numpy's matmul (a library primitive) in float64.
 Readings where the pages are silent (each listed with its reason in the
 design notes): RMS norm without a learned gain, eps 1e-6; modulation as
 (1 + scale) and + shift, one set of six vectors per segment (text, audio,
-video); gate as x + g * branch; GELU with exact erf; biases on every linear;
+video); gate as x + g * branch; GELU with exact erf; SwiGLU as silu(g) * u on
+the stored bf16 gate and up rows; the routing gate as a fourth per-head
+product multiplying the pooled branch, with no activation; biases on every linear;
 half-split RoPE pairs (i, i + d/2) from caller tables; scale d^-1/2 on row and
 tile scores; prefix (text + audio) keys always attended by video rows, top-k
 over video key tiles only; tile-mean divisor = true row count; pooled branch =
@@ -146,15 +148,40 @@ def gelu(z):
     return 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
 
 
-def split_qkv(y, n_heads, head_dim):
+def split_qkv(y, n_heads, head_dim, parts=3):
     """Per-head interleaved projection rows [h][q|k|v][d] (h3.c README, note on
-    the checkpoint's QKV layout) -> q, k, v as [nh][R][d]."""
+    the checkpoint's QKV layout) -> q, k, v as [nh][R][d].  With parts = 4 the
+    fourth block of each head, [h][q|k|v|g][d], is the routing gate g (TensorFold
+    PR #949, "What it adds": q/k/v and the routing gate), returned as a fourth
+    array."""
     R = y.shape[0]
-    t = y.reshape(R, n_heads, 3, head_dim)
-    q = np.ascontiguousarray(t[:, :, 0, :].transpose(1, 0, 2))
-    k = np.ascontiguousarray(t[:, :, 1, :].transpose(1, 0, 2))
-    v = np.ascontiguousarray(t[:, :, 2, :].transpose(1, 0, 2))
-    return q, k, v
+    t = y.reshape(R, n_heads, parts, head_dim)
+    out = [np.ascontiguousarray(t[:, :, i, :].transpose(1, 0, 2)) for i in range(parts)]
+    return tuple(out)
+
+
+def silu(z):
+    """z * sigmoid(z) = z / (1 + e^-z)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def split_gate_up(z, ffn):
+    """FC1 output of the SwiGLU MLP -> (gate, up), each [R][ffn].  The FC1 rows
+    alternate in blocks of 16: rows 32b .. 32b+15 are the gate rows of features
+    16b .. 16b+15 and rows 32b+16 .. 32b+31 their up rows (a storage order of
+    this library's ABI, like the per-head QKV interleave)."""
+    R = z.shape[0]
+    t = z.reshape(R, ffn // 16, 2, 16)
+    return t[:, :, 0, :].reshape(R, ffn), t[:, :, 1, :].reshape(R, ffn)
+
+
+def swiglu_hidden(z, ffn):
+    """h = bf(silu(bf g) * bf u) from the FC1 output z (float64 before rounding):
+    the gate and up products are stored as bf16 like every projection output,
+    then combined in full precision and rounded (TensorFold PR #949, "What it
+    adds": the SwiGLU MLP; the pages' h3_swiglu kernel takes the stored rows)."""
+    g, u = split_gate_up(round_bf16(z), ffn)
+    return round_bf16(silu(g) * u)
 
 
 def qk_norm_rope(u, gain, rope, eps):
@@ -309,15 +336,25 @@ def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=N
       n2 = modnorm(x1; shift2, scale2)
       h  = bf(gelu(n2 W1^T + b1));     f = bf(h W2^T + b2);   x2 = bf(x1 + gate2 * f)
 
+    The pages' own block (sh.mlp = 1, sh.gate = 1) differs in two places: the
+    MLP is SwiGLU, h = bf(silu(bf g) * bf u) with [g | u] = n2 W1^T + b1
+    (split_gate_up), and y carries a fourth per-head block, the routing gate
+    g, which scales the pooled branch of the video rows (o = routed + g *
+    pooled).  The attention width nh * d may differ from the hidden width H
+    (the pages: H = 5,376, 56 heads x 128 = 7,168).
+
     sh: object with n_text, n_audio, n_video, n_heads, head_dim, norm_eps,
-    top_k, pooled.  w: dict of bf16-bit arrays (see synth.block_weights).
-    mod: fp32 [3][6][H].  rope: fp32 [R][d/2][2] or None.  x_in: bf16 bits.
+    top_k, pooled and optionally mlp (0 GELU, 1 SwiGLU), gate (0, 1), ffn.
+    w: dict of bf16-bit arrays (see synth.block_weights).  mod: fp32 [3][6][H].
+    rope: fp32 [R][d/2][2] or None.  x_in: bf16 bits.
     out_rows: None for all rows, else the rows whose attention / x1 / x2 are
     computed (q, k, v and routing always cover all rows).
     timings: None, or a dict that receives the wall time of the all-row part
     ("all_rows") and of the per-row part ("per_row").
     Returns a dict of float64 intermediates (bf16 values where rounded)."""
     t0 = time.perf_counter()
+    mlp = int(getattr(sh, "mlp", 0))
+    use_gate = int(getattr(sh, "gate", 0))
     seg = row_segments(sh.n_text, sh.n_audio, sh.n_video)
     P = sh.n_text + sh.n_audio
     ts = check_tile_map(tile_start, sh.n_text, sh.n_audio, sh.n_video, n_prefix_tiles)
@@ -329,25 +366,31 @@ def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=N
 
     n1 = modulated_rmsnorm(x, shift1, scale1, seg, eps)
     y = round_bf16(linear(n1, f["w_qkv"], f["b_qkv"]))
-    q, k, v = split_qkv(y, sh.n_heads, sh.head_dim)
+    parts = split_qkv(y, sh.n_heads, sh.head_dim, 4 if use_gate else 3)
+    q, k, v = parts[:3]
+    g = parts[3] if use_gate else None
     qt = qk_norm_rope(q, f["q_gain"], rope, eps)
     kt = qk_norm_rope(k, f["k_gain"], rope, eps)
     rt = routing(qt, kt, v, ts, n_prefix_tiles, sh.top_k)
     rows = np.arange(x.shape[0]) if out_rows is None else np.asarray(out_rows)
     t1 = time.perf_counter()
-    a = round_bf16(attention(qt, kt, v, ts, n_prefix_tiles, P, rt, bool(sh.pooled), rows))
+    a = round_bf16(attention(qt, kt, v, ts, n_prefix_tiles, P, rt, bool(sh.pooled), rows, g))
     sr = seg[rows]
     o = round_bf16(linear(a, f["w_o"], f["b_o"]))
     x1 = round_bf16(x[rows] + gate1[sr] * o)
     n2 = modulated_rmsnorm(x1, shift2, scale2, sr, eps)
-    hdn = round_bf16(gelu(linear(n2, f["w_fc1"], f["b_fc1"])))
+    z1 = linear(n2, f["w_fc1"], f["b_fc1"])
+    if mlp == 1:
+        hdn = swiglu_hidden(z1, z1.shape[1] // 2)
+    else:
+        hdn = round_bf16(gelu(z1))
     ff = round_bf16(linear(hdn, f["w_fc2"], f["b_fc2"]))
     x2 = round_bf16(x1 + gate2[sr] * ff)
     if timings is not None:
         timings["all_rows"] = t1 - t0
         timings["per_row"] = time.perf_counter() - t1
-    return dict(rows=rows, n1=n1, y=y, q=qt, k=kt, v=v, attn=a, o=o, x1=x1, n2=n2, h=hdn,
-                f=ff, x2=x2, **rt)
+    return dict(rows=rows, n1=n1, y=y, q=qt, k=kt, v=v, g=g, attn=a, o=o, x1=x1, n2=n2,
+                h=hdn, f=ff, x2=x2, **rt)
 
 
 def final_heads(sh, x, mod_final, head):

@@ -429,3 +429,129 @@ def test_dit_forward_with_identity_blocks_is_heads_only():
     vv, va = O.final_heads(sh, O.bf16_to_f64(x), mf, head)
     np.testing.assert_array_equal(r["vel_video"], vv)
     np.testing.assert_array_equal(r["vel_audio"], va)
+
+
+# ----------------------------------------------------------------------------
+# The pages' own block: SwiGLU MLP, the routing gate, attention width != hidden,
+# cube tiles
+# ----------------------------------------------------------------------------
+
+def test_silu_identities():
+    x = np.linspace(-8, 8, 161)
+    # silu(x) - silu(-x) = x (sigmoid(x) + sigmoid(-x) = 1)
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, rtol=0, atol=1e-14)
+    assert O.silu(0.0) == 0.0
+    # sigmoid(ln 3) = 3/4
+    assert abs(O.silu(math.log(3.0)) - 0.75 * math.log(3.0)) < 1e-15
+    # large arguments: silu(x) -> x, silu(-x) -> 0 from below
+    assert abs(O.silu(40.0) - 40.0) < 1e-12 and -1e-12 < O.silu(-40.0) <= 0.0
+
+
+def test_swiglu_interleave_against_separate_products():
+    """An FC1 weight assembled feature by feature from separate gate and up
+    matrices (gate rows of features 16b..16b+15, then their up rows) gives
+    bf(silu(bf(n Wg^T + bg)) * bf(n Wu^T + bu))."""
+    rng = np.random.default_rng(3)
+    R, H, F = 5, 24, 48
+    n = O.round_bf16(rng.standard_normal((R, H)))
+    wg, wu = O.round_bf16(rng.standard_normal((F, H))), O.round_bf16(rng.standard_normal((F, H)))
+    bg, bu = O.round_bf16(rng.standard_normal(F)), O.round_bf16(rng.standard_normal(F))
+    w1 = np.zeros((2 * F, H)); b1 = np.zeros(2 * F)
+    for f in range(F):
+        blk, j = divmod(f, 16)
+        w1[32 * blk + j] = wg[f]; b1[32 * blk + j] = bg[f]
+        w1[32 * blk + 16 + j] = wu[f]; b1[32 * blk + 16 + j] = bu[f]
+    h = O.swiglu_hidden(O.linear(n, w1, b1), F)
+    g = O.round_bf16(n @ wg.T + bg)
+    u = O.round_bf16(n @ wu.T + bu)
+    expect = O.round_bf16(g * u / (1.0 + np.exp(-g)))
+    np.testing.assert_array_equal(h, expect)
+
+
+def test_routed_attention_gate_ones_and_zeros():
+    from audio_diffusion_transformer_amd import synth as S
+    ts, npt, q, k, v = _small_case()
+    nh, R, d = q.shape
+    sh = S.Shape(5, 7, 40, nh * d, nh, d, 64, tile=8, top_k=2, pooled=1)
+    qb, kb, vb = (O.f64_to_bf16_bits(t) for t in (q, k, v))
+    base = O.routed_attn(sh, ts, npt, qb, kb, vb)
+    ones = O.routed_attn(sh, ts, npt, qb, kb, vb, gate=np.full((nh, R, d), 0x3F80, np.uint16))
+    np.testing.assert_array_equal(ones["out"], base["out"])
+    zero = O.routed_attn(sh, ts, npt, qb, kb, vb, gate=np.zeros((nh, R, d), np.uint16))
+    no_pool = O.routed_attn(sh.replace(pooled=0), ts, npt, qb, kb, vb)
+    np.testing.assert_array_equal(zero["out"], no_pool["out"])
+    # a gate of two doubles the pooled term exactly (before the final rounding)
+    P = sh.n_text + sh.n_audio
+    two = O.routed_attn(sh, ts, npt, qb, kb, vb, gate=np.full((nh, R, d), 0x4000, np.uint16))
+    assert not np.array_equal(two["out"][P:], base["out"][P:])
+    np.testing.assert_array_equal(two["out"][:P], base["out"][:P])
+
+
+def _fasth3_tiny_inputs(seed=11):
+    from audio_diffusion_transformer_amd import synth as S
+    sh = S.Shape(6, 10, 60, 32, 2, 24, 32, tile=16, top_k=3, mlp=1, gate=1,
+                 video_grid=(3, 4, 5), cube=2)
+    ts, npt = S.tile_map(sh)
+    w = S.block_weights(sh, seed=seed)
+    mod = S.modulation(sh, seed=seed)
+    rope = S.rope_tables(sh)
+    x = S.activations(sh, seed=seed, field=True)
+    return sh, ts, npt, w, mod, rope, x
+
+
+def test_fasth3_block_shapes_and_identity():
+    """Attention width 48 != hidden 32, SwiGLU and the gate: zero residual gates
+    still give the identity, byte for byte."""
+    sh, ts, npt, w, mod, rope, x = _fasth3_tiny_inputs()
+    assert w["w_qkv"].shape == (4 * 48, 32) and w["w_o"].shape == (32, 48)
+    assert w["w_fc1"].shape == (64, 32) and w["w_fc2"].shape == (32, 32)
+    r = O.block_forward(sh, ts, npt, w, mod, rope, x)
+    assert r["attn"].shape == (sh.rows, 48) and r["h"].shape == (sh.rows, 32)
+    m0 = mod.copy(); m0[:, 2, :] = 0.0; m0[:, 5, :] = 0.0
+    r0 = O.block_forward(sh, ts, npt, w, m0, rope, x)
+    np.testing.assert_array_equal(O.f64_to_bf16_bits(r0["x2"]), x)
+
+
+def test_fasth3_unit_gate_equals_ungated_block():
+    """With the gate rows of the QKV product zero and their bias 1, g = 1 and the
+    block equals the block without a gate on the same q/k/v rows: this pins the
+    four-part per-head split."""
+    sh, ts, npt, w, mod, rope, x = _fasth3_tiny_inputs()
+    nh, d, H = sh.n_heads, sh.head_dim, sh.hidden
+    wq4 = w["w_qkv"].reshape(nh, 4, d, H).copy()
+    bq4 = w["b_qkv"].reshape(nh, 4, d).copy()
+    wq4[:, 3] = 0
+    bq4[:, 3] = 0x3F80                       # bf16 1.0
+    wg = dict(w, w_qkv=wq4.reshape(-1, H), b_qkv=bq4.reshape(-1))
+    w3 = dict(w, w_qkv=np.ascontiguousarray(wq4[:, :3]).reshape(-1, H),
+              b_qkv=np.ascontiguousarray(bq4[:, :3]).reshape(-1))
+    rg = O.block_forward(sh, ts, npt, wg, mod, rope, x)
+    r3 = O.block_forward(sh.replace(gate=0), ts, npt, w3, mod, rope, x)
+    np.testing.assert_array_equal(rg["x2"], r3["x2"])
+    # and a zero gate equals the block with the pooled branch off
+    bq4[:, 3] = 0
+    wz = dict(w, w_qkv=wq4.reshape(-1, H), b_qkv=bq4.reshape(-1))
+    rz = O.block_forward(sh, ts, npt, wz, mod, rope, x)
+    rp = O.block_forward(sh.replace(gate=0, pooled=0), ts, npt, w3, mod, rope, x)
+    np.testing.assert_array_equal(rz["x2"], rp["x2"])
+
+
+def test_cube_tiles_cover_the_grid():
+    from audio_diffusion_transformer_amd import synth as S
+    sh = S.FASTH3
+    ts, npt = S.tile_map(sh)
+    assert npt == 8 and len(ts) - 1 - npt == 280 and ts[-1] == sh.rows
+    sizes = np.diff(ts[npt:])
+    assert sizes.max() == 64 and sizes.sum() == sh.n_video
+    # the 4x4x4 cube cut of 37 x 15 x 27: edges 1, 3, 3 -> cube sizes are products
+    # of {4, 1} x {4, 3} x {4, 3}
+    assert set(sizes.tolist()) <= {a * b * c for a in (4, 1) for b in (4, 3) for c in (4, 3)}
+    pos = S.video_positions(sh)
+    assert np.array_equal(np.sort(pos), np.arange(sh.n_video))   # a permutation
+    # every tile is one cube: its raster positions span at most 4 frames, rows, columns
+    T, Hh, W = sh.video_grid
+    for i in range(len(sizes)):
+        p = pos[ts[npt + i] - sh.n_prefix:ts[npt + i + 1] - sh.n_prefix]
+        t, h, w = p // (Hh * W), (p // W) % Hh, p % W
+        assert t.max() - t.min() < 4 and h.max() - h.min() < 4 and w.max() - w.min() < 4
+        assert len(p) == (t.max() - t.min() + 1) * (h.max() - h.min() + 1) * (w.max() - w.min() + 1)
