@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libh3.so")
 
 H3_OK, H3_EINVAL, H3_EWORKSPACE, H3_EHIP, H3_EUNSUPPORTED = 0, -1, -2, -3, -4
 H3_WS_BLOCK, H3_WS_DIT, H3_WS_ATTN = 0, 1, 2
+ABI_VERSION = 2  # must match H3_ABI_VERSION in include/h3.h
+
 KERNEL_CLASSES = ["modnorm", "gemm_qkv", "heads", "route", "attn", "gemm_o", "gemm_fc1",
                   "gemm_fc2", "final", "tables"]
 
@@ -29,7 +31,8 @@ class H3Shape(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("ffn", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
                 ("n_prefix_tiles", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("pooled", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
+                ("pooled", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("mlp", ctypes.c_int32), ("gate", ctypes.c_int32)]
 
 
 class H3BlockWeights(ctypes.Structure):
@@ -106,7 +109,7 @@ def make_shape(sh, tile_start, n_prefix_tiles):
     """sh: any object with the fields of synth.Shape."""
     return H3Shape(sh.n_text, sh.n_audio, sh.n_video, sh.hidden, sh.n_heads, sh.head_dim,
                    sh.ffn, len(tile_start) - 1, n_prefix_tiles, sh.top_k, int(sh.pooled),
-                   float(sh.norm_eps))
+                   float(sh.norm_eps), int(getattr(sh, "mlp", 0)), int(getattr(sh, "gate", 0)))
 
 
 def _tiles(tile_start):

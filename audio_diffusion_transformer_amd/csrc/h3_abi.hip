@@ -45,6 +45,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
   h3_shape s;
   int R, P, H, D, F, nh, nT, npt, nQ, nsel, Rp, n_chunks, n_prefix_chunks, nqb, nqb_dense;
+  int A;      // attention width n_heads * head_dim
+  int parts;  // blocks per head in the QKV product: 3, or 4 with the routing gate
+  int F1;     // FC1 output width: F (GELU) or 2F (SwiGLU)
   std::vector<int> tstart, tpstart, chunk_valid, qblocks;
   h3_ws_layout lay;
   size_t off_tstart, off_tpstart, off_chunk, off_qb;
@@ -65,20 +68,24 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
     return fail(H3_EUNSUPPORTED, "head_dim %d not in {64, 128}", s->head_dim);
   p.D = s->head_dim;
   p.nh = s->n_heads;
+  p.A = p.nh * p.D;
   p.H = s->hidden;
+  if (s->mlp != H3_MLP_GELU && s->mlp != H3_MLP_SWIGLU) return fail(H3_EINVAL, "bad mlp %d", s->mlp);
+  if (s->gate != 0 && s->gate != 1) return fail(H3_EINVAL, "gate must be 0 or 1");
+  p.parts = s->gate ? 4 : 3;
+  p.F = s->ffn;
+  p.F1 = s->mlp == H3_MLP_SWIGLU ? 2 * s->ffn : s->ffn;
   if (which != H3_WS_ATTN) {
-    if (p.H != p.nh * p.D) return fail(H3_EINVAL, "hidden %d != n_heads * head_dim", p.H);
     if (p.H % 256 != 0 || p.H > 8192)
       return fail(H3_EUNSUPPORTED, "hidden %d must be a multiple of 256 and <= 8192", p.H);
-    if (s->ffn < 256 || s->ffn % 256 != 0)
-      return fail(H3_EUNSUPPORTED, "ffn %d must be a positive multiple of 256", s->ffn);
-    if (!gemm_shape_ok(p.R, 3 * p.H, p.H) || !gemm_shape_ok(p.R, s->ffn, p.H) ||
-        !gemm_shape_ok(p.R, p.H, s->ffn))
+    if (s->ffn < 128 || s->ffn % 128 != 0 || p.F1 % 256 != 0)
+      return fail(H3_EUNSUPPORTED, "ffn %d: the FC1 width must be a positive multiple of 256", s->ffn);
+    if ((p.parts * p.A) % 256 != 0 || p.A % 128 != 0)
+      return fail(H3_EUNSUPPORTED, "attention width %d: (3 + gate) * width must be a multiple of 256", p.A);
+    if (!gemm_shape_ok(p.R, p.parts * p.A, p.H) || !gemm_shape_ok(p.R, p.H, p.A) ||
+        !gemm_shape_ok(p.R, p.F1, p.H) || !gemm_shape_ok(p.R, p.H, s->ffn))
       return fail(H3_EUNSUPPORTED, "rows x width too large for the GEMM (R*F must stay below 2^31)");
-  } else {
-    p.H = p.nh * p.D;
   }
-  p.F = s->ffn;
   if (!(s->norm_eps >= 0.f)) return fail(H3_EINVAL, "norm_eps must be >= 0");
   p.nT = s->n_tiles;
   p.npt = s->n_prefix_tiles;
@@ -142,10 +149,11 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
   p.off_tpstart = take((size_t)(p.nT + 1) * 4);
   p.off_chunk = take((size_t)p.n_chunks * 4);
   p.off_qb = take((size_t)p.nqb * 16);
-  const size_t R = p.R, H = p.H;
+  const size_t R = p.R, H = p.H, A = p.A;
   if (which != H3_WS_ATTN) {
+    const size_t ywidth = (size_t)p.parts * p.A;  // y (QKV product), then the MLP hidden h
     L.norm = take(R * H * bf);
-    L.big = take(R * (size_t)(3 * p.H > p.F ? 3 * p.H : p.F) * bf);
+    L.big = take(R * (ywidth > (size_t)p.F ? ywidth : (size_t)p.F) * bf);
   }
   L.q = take((size_t)p.nh * p.Rp * p.D * bf);
   L.k = take((size_t)p.nh * p.Rp * p.D * bf);
@@ -157,7 +165,7 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
   L.sel = take((size_t)p.nh * (p.nQ > 0 ? p.nQ : 1) * (p.nsel > 0 ? p.nsel : 1) * 4);
   L.pooled = take((size_t)p.nh * (p.nQ > 0 ? p.nQ : 1) * p.D * f4);
   if (which != H3_WS_ATTN) {
-    L.attn = take(R * H * bf);
+    L.attn = take(R * A * bf);
     L.x1 = take(R * H * bf);
   }
   if (which == H3_WS_DIT) {
@@ -217,13 +225,15 @@ HeadsArgs heads_args(const Plan& p, void* ws) {
   a.nh = p.nh;
   a.nT = p.nT;
   a.npt = p.npt;
-  a.H = p.H;
+  a.parts = p.parts;
+  a.ystride = p.parts * p.A;
   a.eps = p.s.norm_eps;
   return a;
 }
 
+// gate: null, or the routing gate at gate[r * gate_stride + h * gate_hstride + c]
 int run_attention(const Plan& p, void* ws, int32_t* sel_out, float* scores_out, bf16_t* out,
-                  hipStream_t st) {
+                  const bf16_t* gate, int gate_stride, int gate_hstride, hipStream_t st) {
   int* sel = sel_out ? sel_out : at<int>(ws, p.lay.sel);
   float* scores = scores_out ? scores_out : at<float>(ws, p.lay.scores);
   if (p.nQ > 0) {
@@ -255,9 +265,12 @@ int run_attention(const Plan& p, void* ws, int32_t* sel_out, float* scores_out, 
   a.chunk_valid = at<int>(ws, p.off_chunk);
   a.qblocks = at<int4>(ws, p.off_qb);
   a.out = out;
+  a.gate = gate;
+  a.gate_stride = gate_stride;
+  a.gate_hstride = gate_hstride;
   a.nh = p.nh;
   a.Rp = p.Rp;
-  a.H = p.nh * p.D;
+  a.A = p.A;
   a.nT = p.nT;
   a.npt = p.npt;
   a.nQ = p.nQ;
@@ -286,7 +299,7 @@ int check_block_weights(const h3_block_weights* w, int l) {
 // Steps 1-9 of one block; tables already uploaded.
 int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* mod,
               const float* rope, const bf16_t* x_in, bf16_t* x_out, hipStream_t st) {
-  const int R = p.R, H = p.H, F = p.F;
+  const int R = p.R, H = p.H, F = p.F, A = p.A;
   const int nt = p.s.n_text, np_ = p.P;
   bf16_t* norm = at<bf16_t>(ws, p.lay.norm);
   bf16_t* big = at<bf16_t>(ws, p.lay.big);
@@ -305,7 +318,7 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
   e.n_text = nt;
   e.n_prefix = np_;
   prof_begin(H3_K_GEMM_QKV, st);
-  H3_TRY(launch_gemm(EPI_BIAS, norm, w->w_qkv, R, 3 * H, H, e, st));
+  H3_TRY(launch_gemm(EPI_BIAS, norm, w->w_qkv, R, p.parts * A, H, e, st));
   prof_end(H3_K_GEMM_QKV, st);
 
   HeadsArgs ha = heads_args(p, ws);
@@ -317,7 +330,9 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
   H3_TRY(launch_heads(HEADS_QKV, p.D, ha, st));
   prof_end(H3_K_HEADS, st);
 
-  int rc = run_attention(p, ws, nullptr, nullptr, attn, st);
+  // the routing gate: the fourth block of each head's rows of y
+  const bf16_t* gate = p.s.gate ? big + 3 * p.D : nullptr;
+  int rc = run_attention(p, ws, nullptr, nullptr, attn, gate, p.parts * A, p.parts * p.D, st);
   if (rc) return rc;
 
   e = GemmEpi{};
@@ -329,7 +344,7 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
   e.n_text = nt;
   e.n_prefix = np_;
   prof_begin(H3_K_GEMM_O, st);
-  H3_TRY(launch_gemm(EPI_BIAS_RESGATE, attn, w->w_o, R, H, H, e, st));
+  H3_TRY(launch_gemm(EPI_BIAS_RESGATE, attn, w->w_o, R, H, A, e, st));
   prof_end(H3_K_GEMM_O, st);
 
   prof_begin(H3_K_NORM, st);
@@ -341,7 +356,8 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
   e.bias = w->b_fc1;
   e.out = big;
   prof_begin(H3_K_GEMM_FC1, st);
-  H3_TRY(launch_gemm(EPI_BIAS_GELU, norm, w->w_fc1, R, F, H, e, st));
+  H3_TRY(launch_gemm(p.s.mlp == H3_MLP_SWIGLU ? EPI_BIAS_SWIGLU : EPI_BIAS_GELU, norm, w->w_fc1,
+                     R, p.F1, H, e, st));
   prof_end(H3_K_GEMM_FC1, st);
 
   e = GemmEpi{};
@@ -500,9 +516,9 @@ int h3_routed_attn(const h3_shape* shape, const int32_t* tile_start, const h3_bf
   int rc = make_plan(shape, tile_start, H3_WS_ATTN, p);
   if (rc) return rc;
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
-  if (gate) return fail(H3_EUNSUPPORTED, "a gated pooled branch is not supported");
   if (!q || !k || !v || !out) return fail(H3_EINVAL, "q, k, v and out are required");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (gate && !aligned16(gate)))
     return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   if ((rc = upload_tables(p, ws, st))) return rc;
@@ -513,7 +529,7 @@ int h3_routed_attn(const h3_shape* shape, const int32_t* tile_start, const h3_bf
   prof_begin(H3_K_HEADS, st);
   H3_TRY(launch_heads(HEADS_SPLIT, p.D, ha, st));
   prof_end(H3_K_HEADS, st);
-  return run_attention(p, ws, sel, scores, out, st);
+  return run_attention(p, ws, sel, scores, out, gate, p.A, p.D, st);
 }
 
 int h3_prof_enable(int on) {

@@ -23,10 +23,10 @@ hipError_t launch_modnorm(const bf16_t* x, bf16_t* out, int out_row0, const floa
                           int n_text, int n_prefix, float eps, hipStream_t s);
 
 // ---- GEMM: C[M][N] = A[M][K] * B[N][K]^T with a fused epilogue -------------
-enum { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESGATE = 2 };
+enum { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESGATE = 2, EPI_BIAS_SWIGLU = 3 };
 struct GemmEpi {
   const bf16_t* bias;   // [N]
-  bf16_t* out;          // [M][N]
+  bf16_t* out;          // [M][N]; EPI_BIAS_SWIGLU: [M][N/2]
   const bf16_t* res;    // [M][N] residual input (EPI_BIAS_RESGATE)
   const float* gate;    // gate of segment s, column n at gate[s * gate_seg_stride + n]
   int gate_seg_stride;
@@ -55,7 +55,9 @@ struct HeadsArgs {
   float* vbar;           // [nh][nT][d]
   const int* tstart;     // [nT+1] real rows
   const int* tpstart;    // [nT+1] padded rows
-  int R, Rp, nh, nT, npt, H;
+  int R, Rp, nh, nT, npt;
+  int parts;             // MODE_QKV: blocks per head in y, 3 ([q|k|v]) or 4 ([q|k|v|g])
+  int ystride;           // MODE_QKV: elements per row of y (parts * nh * d)
   float eps;
 };
 enum { HEADS_QKV = 0, HEADS_SPLIT = 1 };
@@ -84,8 +86,11 @@ struct AttnArgs {
   const int* tpstart;       // [nT+1]
   const int* chunk_valid;   // [Rp/32]
   const int4* qblocks;      // [nqb]: (tile, padded row0, nrows, real row0)
-  bf16_t* out;              // [R][H]
-  int nh, Rp, H, nT, npt, nQ, nsel, nqb, nqb_dense, n_prefix_chunks, n_chunks;
+  bf16_t* out;              // [R][A]
+  const bf16_t* gate;       // null, or the routing gate of row r, head h, column c at
+                            // gate[r * gate_stride + h * gate_hstride + c]
+  int gate_stride, gate_hstride;
+  int nh, Rp, A, nT, npt, nQ, nsel, nqb, nqb_dense, n_prefix_chunks, n_chunks;
 };
 bool attn_shape_ok(int n_chunks, int nsel);
 hipError_t launch_attn(int head_dim, const AttnArgs& a, hipStream_t s);

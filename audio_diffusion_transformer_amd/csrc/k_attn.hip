@@ -6,8 +6,9 @@
 // rounded to bf16 before the value product) and the parity notes (the audio
 // rows attend densely).  A video row of query tile i attends the prefix rows,
 // then the rows of the selected tiles sel[h][i] in ascending order, and gets
-// the fp32 pooled branch pooled[h][i] added before the bf16 rounding; a text
-// or audio row attends every row.
+// the fp32 pooled branch pooled[h][i] (times the routing gate g of the row,
+// when one is given: "What it adds", q/k/v and the routing gate) added before
+// the bf16 rounding; a text or audio row attends every row.
 //
 // Operands (written by the head-layout kernel): q, k [nh][Rp][D] and v^T
 // [nh][D][Rp] in a padded row space where every tile starts on a multiple of
@@ -356,21 +357,26 @@ void k_attn(AttnArgs a) {
   const float* pooled = (!dense && a.pooled)
                             ? a.pooled + ((size_t)h * a.nQ + (tile - a.npt)) * D
                             : nullptr;
+  const bool gated = pooled && a.gate;  // routed + g * pooled
   for (int idx = tid; idx < 64 * (D / 8); idx += 256) {
     const int qq = idx / (D / 8), d8 = (idx % (D / 8)) * 8;
     if (qq >= nrows) continue;
     const float inv = 1.0f / sLt[qq];
+    u32x4_t gw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
+    if (gated)
+      gw = *reinterpret_cast<const u32x4_t*>(
+          a.gate + (size_t)(row0 + qq) * a.gate_stride + h * a.gate_hstride + d8);
     u32x4_t w;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float x0 = sO[qq][d8 + 2 * t] * inv, x1 = sO[qq][d8 + 2 * t + 1] * inv;
       if (pooled) {
-        x0 += pooled[d8 + 2 * t];
-        x1 += pooled[d8 + 2 * t + 1];
+        x0 = fmaf(bflo(gw[t]), pooled[d8 + 2 * t], x0);
+        x1 = fmaf(bfhi(gw[t]), pooled[d8 + 2 * t + 1], x1);
       }
       w[t] = pack2(x0, x1);
     }
-    *reinterpret_cast<u32x4_t*>(a.out + (size_t)(row0 + qq) * a.H + h * D + d8) = w;
+    *reinterpret_cast<u32x4_t*>(a.out + (size_t)(row0 + qq) * a.A + h * D + d8) = w;
   }
 }
 

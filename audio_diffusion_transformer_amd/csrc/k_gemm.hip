@@ -42,6 +42,8 @@
 //   EPI_BIAS:         C = bf(acc + bias)
 //   EPI_BIAS_GELU:    C = bf(gelu(acc + bias)),  gelu(z) = z/2 (1 + erf(z/sqrt2)) (gelu_erf below)
 //   EPI_BIAS_RESGATE: C = bf(res + gate[seg(row)] * bf(acc + bias))
+//   EPI_BIAS_SWIGLU:  C[., f] = bf(silu(bf(acc_g + bias_g)) bf(acc_u + bias_u)), the gate and
+//                     up columns of feature f interleaved in blocks of 16 (C is N/2 wide)
 #include "common.h"
 #include "internal.h"
 
@@ -236,6 +238,41 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
   // column l%16 of that 16x16 block.  Each wave rounds its 128x64 sub-tile into
   // its own 16 KB of LDS, then writes it back in 16-byte chunks.
   bf16_t* st = smem + wave * (128 * 64);
+  if constexpr (EPI == EPI_BIAS_SWIGLU) {
+    // GEMM columns 32b .. 32b+15 are the gate values of features 16b .. 16b+15
+    // and 32b+16 .. 32b+31 their up values, so blocks j = 2jj (gate) and
+    // 2jj + 1 (up) of a lane hold the same feature: h = bf(silu(bf g) bf u).
+    // The wave's 64 GEMM columns give 32 output columns (128 x 32 in LDS).
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int ncol = n0 + wn * 64 + jj * 32 + l16;
+      const float bg = bf2f(ep.bias[ncol]), bu = bf2f(ep.bias[ncol + 16]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = i * 16 + 4 * q4 + e;
+          const float g = bf2f(f2bf(acc[i][2 * jj][e] + bg));
+          const float u = bf2f(f2bf(acc[i][2 * jj + 1][e] + bu));
+          const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+          st[r * 32 + jj * 16 + l16] = f2bf(g * sig * u);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const int NO = N / 2;  // output width
+#pragma unroll 4
+    for (int t = 0; t < 8; ++t) {
+      const int q = t * 64 + lane;
+      const int r = q >> 2, c8 = (q & 3) * 8;
+      const int row = m0 + wm * 128 + r;
+      if (row >= M) continue;
+      const int col = (n0 + wn * 64) / 2 + c8;
+      *reinterpret_cast<u32x4_t*>(ep.out + (size_t)row * NO + col) =
+          *reinterpret_cast<const u32x4_t*>(st + r * 32 + c8);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float bias = bf2f(ep.bias[n0 + wn * 64 + j * 16 + l16]);
@@ -293,6 +330,9 @@ hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, 
       break;
     case EPI_BIAS_GELU:
       hipLaunchKernelGGL(k_gemm_bf16<EPI_BIAS_GELU>, grid, block, 0, s, A, B, M, N, K, ep);
+      break;
+    case EPI_BIAS_SWIGLU:
+      hipLaunchKernelGGL(k_gemm_bf16<EPI_BIAS_SWIGLU>, grid, block, 0, s, A, B, M, N, K, ep);
       break;
     default:
       hipLaunchKernelGGL(k_gemm_bf16<EPI_BIAS_RESGATE>, grid, block, 0, s, A, B, M, N, K, ep);

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
 
   auto src_of = [&](int which, int row) -> const bf16_t* {
     if constexpr (MODE == HEADS_QKV)
-      return a.y + (size_t)row * (3 * a.H) + h * 3 * D + which * D + 8 * u;
+      return a.y + (size_t)row * a.ystride + h * a.parts * D + which * D + 8 * u;
     else
       return (which == 0 ? a.q_in : which == 1 ? a.k_in : a.v_in) + ((size_t)h * a.R + row) * D +
              8 * u;
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (rl < len) {
         if constexpr (MODE == HEADS_QKV)
-          w = *reinterpret_cast<const u32x4_t*>(a.y + (size_t)(r_beg + rl) * (3 * a.H) +
-                                                 h * 3 * D + 2 * D + 8 * uu);
+          w = *reinterpret_cast<const u32x4_t*>(a.y + (size_t)(r_beg + rl) * a.ystride +
+                                                 h * a.parts * D + 2 * D + 8 * uu);
         else
           w = *reinterpret_cast<const u32x4_t*>(a.v_in + ((size_t)h * a.R + r_beg + rl) * D +
                                                  8 * uu);

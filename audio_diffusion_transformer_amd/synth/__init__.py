@@ -150,10 +150,11 @@ CONFIGS = {"tiny": TINY, "mid": MID, "full": FULL}
 # SwiGLU 14,336, the routing gate; 36 text / 414 audio / 14,985 video rows, the
 # video a 37 x 15 x 27 grid cut into 4 x 4 x 4 cubes (280 video tiles, 8 prefix
 # tiles), top-k 56.  FASTH3_TINY keeps every feature at a size the oracle runs in
-# seconds (a 5 x 6 x 7 video grid, 3 x 3 x 3 cubes: 24 ragged video tiles).
+# seconds: hidden 256 with 6 heads x 64 (384), a 5 x 6 x 7 video grid in
+# 3 x 3 x 3 cubes (12 ragged video tiles).
 FASTH3 = Shape(36, 414, 14985, 5376, 56, 128, 14336, tile=64, top_k=56, mlp=1, gate=1,
                video_grid=(37, 15, 27), cube=4)
-FASTH3_TINY = Shape(20, 50, 210, 256, 4, 64, 512, tile=64, top_k=6, mlp=1, gate=1,
+FASTH3_TINY = Shape(20, 50, 210, 256, 6, 64, 512, tile=64, top_k=6, mlp=1, gate=1,
                     video_grid=(5, 6, 7), cube=3)
 
 

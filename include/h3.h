@@ -61,26 +61,38 @@ enum {
 
 enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2 };
 
-#define H3_ABI_VERSION 1
+#define H3_ABI_VERSION 2
 
 typedef struct {
   int32_t n_text, n_audio, n_video;  /* packed in this order */
-  int32_t hidden;                    /* H = n_heads * head_dim; multiple of 256, <= 8192 */
-  int32_t n_heads, head_dim;         /* head_dim in {64, 128} */
+  int32_t hidden;                    /* H: multiple of 256, <= 8192 */
+  int32_t n_heads, head_dim;         /* head_dim in {64, 128}; attention width A = n_heads * head_dim
+                                        (may differ from H; (3 + gate) A a multiple of 256) */
   int32_t ffn;                       /* F, multiple of 256 */
   int32_t n_tiles, n_prefix_tiles;   /* tile map size (<= 2048); prefix tiles cover rows [0, P) */
   int32_t top_k;                     /* video key tiles per (head, video query tile); >= nQ keeps all;
                                         min(top_k, nQ) <= 512 */
   int32_t pooled;                    /* 1: add the pooled branch to video rows */
   float norm_eps;                    /* eps of the RMS norms (activation and Q/K) */
+  int32_t mlp;                       /* H3_MLP_GELU or H3_MLP_SWIGLU */
+  int32_t gate;                      /* 1: the QKV product has a fourth per-head block, the routing
+                                        gate g, and video rows get routed + g * pooled */
 } h3_shape;
+
+/* MLP of the block.  GELU: h = bf(gelu(n2 W1^T + b1)), W1 [F][H].
+ * SwiGLU (TensorFold PR #949, "What it adds": the SwiGLU MLP): W1 [2F][H] whose
+ * rows alternate in blocks of 16 (rows 32b .. 32b+15: gate rows of features
+ * 16b .. 16b+15; rows 32b+16 .. 32b+31: their up rows), b1 likewise;
+ * h = bf(silu(bf(g)) * bf(u)), silu(z) = z / (1 + e^-z). */
+enum { H3_MLP_GELU = 0, H3_MLP_SWIGLU = 1 };
 
 /* One block's weights, all bf16, device pointers. */
 typedef struct {
-  const h3_bf16 *w_qkv, *b_qkv;  /* [3H][H], [3H]; output rows per head interleaved [h][q|k|v][d] */
+  const h3_bf16 *w_qkv, *b_qkv;  /* [(3 + gate) A][H], [(3 + gate) A]; output rows per head
+                                    interleaved [h][q|k|v][d], or [h][q|k|v|g][d] with the gate */
   const h3_bf16 *q_gain, *k_gain;/* [d] each: gains of the per-head Q/K RMS norm */
-  const h3_bf16 *w_o, *b_o;      /* [H][H], [H] */
-  const h3_bf16 *w_fc1, *b_fc1;  /* [F][H], [F] */
+  const h3_bf16 *w_o, *b_o;      /* [H][A], [H] */
+  const h3_bf16 *w_fc1, *b_fc1;  /* [F][H], [F]; SwiGLU: [2F][H], [2F] (see H3_MLP_SWIGLU) */
   const h3_bf16 *w_fc2, *b_fc2;  /* [H][F], [H] */
 } h3_block_weights;
 
@@ -132,6 +144,10 @@ int h3_workspace_layout(const h3_shape* shape, const int32_t* tile_start, int32_
  *   x1 = bf(x + gate1[seg] bf(attn Wo^T + bo))
  *   n2 = bf(x1 rms(x1)^-1 (1 + scale2[seg]) + shift2[seg])
  *   x2 = bf(x1 + gate2[seg] bf(bf(gelu(n2 W1^T + b1)) W2^T + b2))
+ * With shape->mlp = H3_MLP_SWIGLU the MLP hidden row is bf(silu(bf g) bf u)
+ * (see H3_MLP_SWIGLU); with shape->gate = 1 the video rows' attention output is
+ * bf(routed + g pooled), g the fourth per-head block of y (TensorFold PR #949,
+ * "What it adds": q/k/v and the routing gate, the pooled branch).
  * mod:  fp32 [3 segments][6][H], vectors (shift1, scale1, gate1, shift2, scale2, gate2).
  * rope: fp32 [R][d/2][2] (cos, sin) for the pairs (i, i + d/2), or NULL (no rotation).
  * x_in, x_out: [R][H] bf16.  Workspace: H3_WS_BLOCK. */
@@ -156,7 +172,8 @@ int h3_dit_forward(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_
 /* Routed attention alone on head-major q, k, v ([nh][R][d] bf16): tile
  * means, scores, top-k, pooled branch and attention as in h3_block_forward.
  *   out:    [R][nh*d] bf16.
- *   gate:   must be NULL (a gated pooled branch is not supported yet).
+ *   gate:   NULL, or [R][nh*d] bf16: video rows get routed + gate * pooled
+ *           (fp32, then the bf16 rounding); text and audio rows ignore it.
  *   sel:    NULL or int32 [nh][nQ][min(top_k, nQ)]: selected tile ids, ascending.
  *   scores: NULL or fp32 [nh][nQ][n_tiles]: the tile scores.
  * Workspace: H3_WS_ATTN. */

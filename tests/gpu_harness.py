@@ -67,7 +67,7 @@ class BlockRun:
         r["scores"] = view(lay.scores, np.float32, (nh, nQ, nT)).astype(np.float64)
         r["sel"] = view(lay.sel, np.int32, (nh, nQ, nsel))
         r["pooled"] = view(lay.pooled, np.float32, (nh, nQ, d)).astype(np.float64)
-        r["attn"] = b2f(view(lay.attn, np.uint16, (R, H)))
+        r["attn"] = b2f(view(lay.attn, np.uint16, (R, nh * d)))
         r["x1"] = b2f(view(lay.x1, np.uint16, (R, H)))
         r["n2"] = b2f(view(lay.norm, np.uint16, (R, H)))
         r["h"] = b2f(view(lay.big, np.uint16, (R, sh.ffn)))

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.h3_abi_version() == 1
+    assert lib.h3_abi_version() == 2
 
 
 def _shape(sh):
@@ -62,7 +62,10 @@ def test_workspace_layout_is_consistent(lib):
 
 @pytest.mark.parametrize("mutate,code", [
     (lambda s, t: setattr(s, "head_dim", 96), B.H3_EUNSUPPORTED),
-    (lambda s, t: setattr(s, "hidden", 300), B.H3_EINVAL),
+    (lambda s, t: setattr(s, "hidden", 300), B.H3_EUNSUPPORTED),
+    (lambda s, t: setattr(s, "mlp", 2), B.H3_EINVAL),
+    (lambda s, t: setattr(s, "gate", 3), B.H3_EINVAL),
+    (lambda s, t: setattr(s, "n_heads", 3), B.H3_EUNSUPPORTED),   # 3 x 64 x 3 not a multiple of 256
     (lambda s, t: setattr(s, "ffn", 1000), B.H3_EUNSUPPORTED),
     (lambda s, t: setattr(s, "n_prefix_tiles", 1), B.H3_EINVAL),
     (lambda s, t: t.__setitem__(3, t[2]), B.H3_EINVAL),
@@ -100,11 +103,26 @@ def test_entry_points_validate_before_launch(lib):
     rc = lib.h3_routed_attn(ctypes.byref(shape), tp, None, None, None, None, None, None, None,
                             ctypes.c_void_p(256), 1 << 40, None)
     assert rc == B.H3_EINVAL
+    # a misaligned gate is refused on the host (no launch)
     rc = lib.h3_routed_attn(ctypes.byref(shape), tp, ctypes.c_void_p(256), ctypes.c_void_p(256),
-                            ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                            ctypes.c_void_p(256), ctypes.c_void_p(258), ctypes.c_void_p(256),
                             None, None, ctypes.c_void_p(256), 1 << 40, None)
-    assert rc == B.H3_EUNSUPPORTED   # a gate is not supported
+    assert rc == B.H3_EINVAL and "aligned" in B.last_error()
     hw = B.H3HeadWeights()
     rc = lib.h3_dit_forward(ctypes.byref(shape), 1, tp, None, ctypes.byref(hw), None, None, None,
                             None, None, None, ctypes.c_void_p(256), 1 << 40, None)
     assert rc == B.H3_EINVAL
+
+
+def test_pages_block_shapes_are_accepted(lib):
+    """Attention width != hidden, SwiGLU and the routing gate (the pages' block):
+    the plan sizes y as (3 + gate) A, the attention output as A and the MLP
+    hidden as F."""
+    for sh in (S.FASTH3_TINY, S.FASTH3):
+        shape, ts = _shape(sh)
+        lay = B.workspace_layout(shape, ts, B.H3_WS_BLOCK)
+        R, H, A, F = sh.rows, sh.hidden, sh.attn_width, sh.ffn
+        assert lay.big - lay.norm >= R * H * 2
+        big_bytes = lay.q - lay.big
+        assert big_bytes >= R * max(4 * A, F) * 2
+        assert lay.x1 - lay.attn >= R * A * 2
