@@ -7,6 +7,11 @@ the pooled branch, random-init bf16 weights, then the final norm and the
 video / audio heads.  One "step" is one forward with that step's fresh
 modulation tables.  Inputs are resident in HBM before the timed region.
 
+--workload fasth3 runs the same forward with the pages' own block and
+geometry instead: hidden 5376, 56 heads x 128, SwiGLU FFN 14336, the
+per-head routing gate on the pooled branch, 36 text / 414 audio rows and a
+37 x 15 x 27 video grid cut into 4 x 4 x 4 cubes (280 tiles), top-k 56.
+
 Prints one JSON line.  Besides the time per forward it reports, for the
 dominant kernel, the achieved fraction of its roofline (algorithmic FLOP per
 launch over the launch's average duration, from HIP events recorded around
@@ -29,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 N_BLOCKS = 50
+PAGES_FASTH3_S = 10.1       # the pages' 50-block FastH3 forward, median of steps 2-8, M5 Ultra
 
 
 def parse():
@@ -39,6 +45,10 @@ def parse():
     ap.add_argument("--blocks", type=int, default=N_BLOCKS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prof", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--workload", choices=["full", "fasth3"], default="full",
+                    help="full: the default 50-block forward (hidden 5120, GELU); fasth3: the "
+                         "pages' own block and geometry (hidden 5376, 56x128 heads, SwiGLU "
+                         "14336, routing gate, cube tiles, top-k 56)")
     ap.add_argument("--attn-sweep", action="store_true",
                     help="only time h3_routed_attn at 15,435 rows x 40 heads x 128 over tile "
                          "size {32, 64, 128} x top-k {8, 32, all}; one JSON line per case")
@@ -59,16 +69,19 @@ TRAFFIC = {
     "sources": ["audio_diffusion_transformer_amd/csrc/k_gemm.hip",
                 "audio_diffusion_transformer_amd/csrc/common.h",
                 "audio_diffusion_transformer_amd/csrc/internal.h"],
-    "sources_sha256": "b9e1debff0f81bf711672e4760dbfe2cd0d4ea88d3a884b93fe394c37157ca87",
+    "sources_sha256": "ec45c21f772d6ad65560689a29595d2eb5798fe67a80a98cea1404411b5e12e9",
     # raw KiB per dispatch and the copy's scale factors (1 GiB copy: FETCH_SIZE
     # 524294.5 KiB, WRITE_SIZE 1048576.0 KiB)
-    "fetch_kib": 2563252.5, "fetch_scale": 1.999975,
+    "fetch_kib": 2583991.75, "fetch_scale": 1.999975,
     "write_kib": 617400.0, "write_scale": 1.000000,
 }
 
 
+WORKLOAD = "full"
+
+
 def measured_traffic(kernel):
-    if TRAFFIC is None or TRAFFIC["kernel"] != kernel:
+    if TRAFFIC is None or TRAFFIC["kernel"] != kernel or WORKLOAD != "full":
         return None
     import hashlib
     h = hashlib.sha256()
@@ -157,12 +170,14 @@ def copy_calibration():
 def kernel_work(sh, ts, npt, plan_sel_rows):
     """Algorithmic FLOP (GEMMs, attention) and bytes (norm) per launch."""
     R, H, F, nh, d = sh.rows, sh.hidden, sh.ffn, sh.n_heads, sh.head_dim
-    P = sh.n_prefix
+    A = nh * d                      # attention width
+    parts = 4 if sh.gate else 3     # per-head blocks of the QKV product
+    F1 = 2 * F if sh.mlp == 1 else F
     keys = plan_sel_rows            # total keys over all query rows, per head
     return {
-        "gemm_qkv": ("mfma", 2.0 * R * 3 * H * H),
-        "gemm_o": ("mfma", 2.0 * R * H * H),
-        "gemm_fc1": ("mfma", 2.0 * R * F * H),
+        "gemm_qkv": ("mfma", 2.0 * R * parts * A * H),
+        "gemm_o": ("mfma", 2.0 * R * H * A),
+        "gemm_fc1": ("mfma", 2.0 * R * F1 * H),
         "gemm_fc2": ("mfma", 2.0 * R * H * F),
         "attn": ("mfma", 4.0 * d * nh * keys),
         # modnorm: read x [R][H] bf16, write n [R][H] bf16
@@ -238,7 +253,9 @@ def main():
     from audio_diffusion_transformer_amd import synth as S
     from audio_diffusion_transformer_amd import tensors as T
 
-    sh = S.FULL
+    global WORKLOAD
+    WORKLOAD = args.workload
+    sh = S.FASTH3 if args.workload == "fasth3" else S.FULL
     L = args.blocks
     ts, npt = S.tile_map(sh)
     shape = B.make_shape(sh, ts, npt)
@@ -325,7 +342,9 @@ def main():
 
     srt = sorted(step_ms)
     line = {
-        "metric": "s per 50-block DiT forward at 15,435 rows; GEMM/attn % of bf16 MFMA peak",
+        "metric": ("s per 50-block DiT forward at 15,435 rows; GEMM/attn % of bf16 MFMA peak"
+                   if args.workload == "full" else
+                   "s per 50-block FastH3 forward at 15,435 rows (the pages' block and geometry)"),
         "value": round(ms_per_step / 1e3, 5),
         "unit": "s",
         "n_gpus": 1,
@@ -334,13 +353,21 @@ def main():
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": None,
+        # the pages time this same forward (FastH3 geometry, 50 blocks) at 10.1 s
+        # on an Apple M5 Ultra: another machine, a ratio for context only
+        "vs_baseline": (round(ms_per_step / 1e3 / PAGES_FASTH3_S, 4)
+                        if args.workload == "fasth3" else None),
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": (f"{L}-block H3-style DiT forward, 15,435 rows (512 text / 543 "
                                 f"audio / 14,380 video), hidden 5120, 40x128 heads, GELU FFN "
                                 f"20480, tile 64, top-k 32 + pooled, heads 96/32, seeded "
-                                f"random bf16 weights"),
+                                f"random bf16 weights" if args.workload == "full" else
+                                f"{L}-block FastH3 forward, 15,435 rows (36 text / 414 audio / "
+                                f"14,985 video as a 37x15x27 grid in 4x4x4 cubes: 8 + 280 "
+                                f"tiles), hidden 5376, 56x128 heads, SwiGLU FFN 14336, "
+                                f"routing gate, top-k 56 + pooled, heads 96/32, seeded random "
+                                f"bf16 weights"),
                    "blocks": L, "rows": sh.rows, "hidden": sh.hidden, "ffn": sh.ffn,
                    "tile": sh.tile, "top_k": sh.top_k},
         "step_ms": [round(s, 2) for s in step_ms],
