@@ -15,24 +15,27 @@
 // 32 rows; a 32-row "chunk" therefore never straddles two tiles, and
 // chunk_valid[c] gives its number of real rows.
 //
-// One workgroup (4 wave64) per (64-row query block, head).  Every wave takes
-// all 64 queries and every 4th key chunk of the block's key list.  Each wave
-// streams its chunks (K rows and the matching v^T columns, 2 x 32 x D bf16)
-// into its own two LDS buffers with global_load_lds_dwordx4, one chunk ahead
-// of the one it computes; the buffers are XOR-swizzled so that the 16-byte
-// fragment reads below are free of bank conflicts.  No workgroup barrier is
-// needed inside the loop: each wave waits only for its own loads.
-//   S^T (32 keys x 32 queries) = K (32 x D) * Q^T (D x 32)   v_mfma_f32_32x32x16_bf16
-// The MFMA result holds, in lane l, query l%32 and keys 8(e/4) + 4(l/32) + e%4
-// (e < 16).  That is also the B-operand layout the value product needs:
-//   O^T (D x 32 queries) += V^T (D x 16 keys) * P^T (16 keys x 32 queries)
-// with the 8 key slots of lane l taken as elements e = 8m..8m+7 of S^T, so
-// the probabilities never leave their lanes; v^T is stored with the middle two
-// 4-key blocks of every 16-key group swapped, so the matching 8 keys of V^T
-// (16m + 4(l/32) + {0..3, 8..11}) are one 16-byte run.  Each lane thus owns one query per
-// 32-query half: the running max / sum need one exchange with lane l^32.
-// Scores are scaled into the log2 domain (exp2).  At the end the four waves'
-// (max, sum, O) are combined in LDS in a fixed wave order.
+// One workgroup (4 wave64) per (64-row query block, head); wave w owns the 16
+// queries 16w .. 16w+15 of the block, and all four waves walk the block's key
+// list one 32-key chunk at a time.  Each chunk (K rows and the matching v^T
+// columns, 2 x 32 x D bf16) is streamed into a two-stage LDS ring with
+// global_load_lds_dwordx4 (waves 0-1 move K, waves 2-3 move v^T), one chunk
+// ahead of the one computed; the ring is XOR-swizzled so that the 16-byte
+// fragment reads below are free of bank conflicts.  With 16 queries per wave
+// a workgroup needs about 35 KB of LDS and few registers, so four workgroups
+// share a CU and every SIMD holds four waves: one wave's softmax runs while
+// another's products occupy the matrix core.
+//   S^T (32 keys x 16 queries) = K (32 x D) Q^T (D x 16)      v_mfma_f32_16x16x32_bf16
+// computed as two 16-key blocks kb; lane l holds query l%16 and keys
+// 16 kb + 4(l/16) + e (e < 4).  Those 8 scores, rounded to bf16, are exactly
+// the lane's B operand of the value product
+//   O^T (D x 16 queries) += V^T (D x 32 keys) P^T (32 keys x 16 queries)
+// when the contraction slot 8(l/16) + j stands for key 4(l/16) + j (j < 4) or
+// 16 + 4(l/16) + j - 4 (j >= 4): v^T stores the eight 4-key blocks of every
+// 32-key chunk in the order 0, 4, 1, 5, 2, 6, 3, 7, so the matching keys of a
+// V^T row are one 16-byte run.  The probabilities never leave their lanes;
+// the four lanes that share a query exchange the running max with two
+// shuffles.  Scores are scaled into the log2 domain (exp2).
 #include "common.h"
 #include "internal.h"
 
@@ -48,6 +51,28 @@ __device__ __forceinline__ bf16x8_t pack8(const float* p) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) w[t] = pack2(p[2 * t], p[2 * t + 1]);
   return as_bf16x8(w);
+}
+
+// The value of lanes l ^ 16 (and l ^ 32) through the gfx950 lane-swap
+// instructions: with both operands equal, v_permlane16_swap returns rows
+// (r0, r0, r2, r2) and (r1, r1, r3, r3) of 16 lanes, v_permlane32_swap
+// (lo, lo) and (hi, hi), so max / sum of the pair is the xor-16 (xor-32)
+// reduction, computed in the same operand order in every lane.
+__device__ __forceinline__ float max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
@@ -71,23 +96,25 @@ __device__ __forceinline__ int swz_k(int row) {
 __device__ __forceinline__ int swz_v(int d) { return (d >> 2) & 3; }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_attn(AttnArgs a) {
-  constexpr int NDC = D / 16;  // 16-wide d slices of the score product
-  constexpr int NDB = D / 32;  // 32-row d blocks of the value product
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_attn(AttnArgs a) {
+  constexpr int NDS = D / 32;  // 32-wide d steps of the score product
+  constexpr int NDB = D / 16;  // 16-row d blocks of the value product
   constexpr int U = D / 8;     // 16-byte units per K row
   constexpr int CH = 32 * D;   // bf16 elements of a K chunk (and of a v^T chunk)
   constexpr int STG = 2 * CH;  // one stage: K chunk then v^T chunk
-  constexpr int NDMA = D / 16; // 1 KB loads per lane for a K (or a v^T) chunk
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * 2 * STG];  // [stream][stage]
-  __shared__ int sOff[kMaxSelAttn + 1];
-  __shared__ int sC0[kMaxSelAttn];
-  __shared__ uint8_t sValid[kMaxChunks];  // real rows of every 32-row key chunk
-  __shared__ float sM[2][64], sL[2][64], sLt[64];
+  constexpr int NDMA = D / 32; // 1 KB loads per lane and chunk
+  constexpr int SO = D + 4;    // fp32 row stride of the output staging
+  constexpr int RING = 2 * STG * 2, OSTG = 64 * SO * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[RING > OSTG ? RING : OSTG];
+  // dynamic: chunk starts and key-list offsets of the selected tiles, then the
+  // valid-row counts of every chunk
+  extern __shared__ __attribute__((aligned(16))) int dyn[];
+  int* const sOff = dyn;                    // [nsel + 1]
+  int* const sC0 = dyn + a.nsel + 1;        // [nsel]
+  uint8_t* const sValid = reinterpret_cast<uint8_t*>(dyn + 2 * a.nsel + 1);  // [n_chunks]
+  bf16_t* const ring = reinterpret_cast<bf16_t*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qh = wave & 1;   // query half (rows 32 qh .. 32 qh + 31 of the block)
-  const int str = wave >> 1; // key stream: chunks str, str + 2, str + 4, ...
   // Work order.  Dense query blocks first (they are the long ones), then video
   // blocks.  Workgroup ids are dealt round-robin over the 8 XCDs; when the head
   // count is a multiple of 8, head h is given to XCD h % 8 (XCD x runs the
@@ -119,7 +146,7 @@ void k_attn(AttnArgs a) {
   }
   const int4 qb = a.qblocks[qbi];
   const int tile = qb.x, prow0 = qb.y, nrows = qb.z, row0 = qb.w;
-  const bool q_live = qh * 32 < nrows;  // this wave's query half holds real rows
+  const bool q_live = wave * 16 < nrows;  // this wave's 16 queries hold real rows
   const bool dense = tile < a.npt;
 
   for (int c = tid; c < a.n_chunks; c += 256) sValid[c] = (uint8_t)a.chunk_valid[c];
@@ -178,40 +205,38 @@ void k_attn(AttnArgs a) {
   };
 
   const size_t Rp = (size_t)a.Rp;
-  const int l32 = lane & 31, g = lane >> 5;
+  const int l16 = lane & 15, g = lane >> 4;
 
-  // Q^T fragments (B operand): query l%32 of this wave's half, d = 16c + 8g .. +7.
-  bf16x8_t qf[NDC];
+  // Q^T fragments (B operand): query 16 wave + l%16, d = 32 s + 8g .. +7.
+  bf16x8_t qf[NDS];
   {
-    const int r = qh * 32 + l32;
+    const int r = wave * 16 + l16;
     const bf16_t* qp = a.q + ((size_t)h * Rp + prow0 + r) * D + 8 * g;
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
+    for (int c = 0; c < NDS; ++c) {
       u32x4_t w = {0u, 0u, 0u, 0u};
-      if (r < nrows) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * c);
+      if (r < nrows) w = *reinterpret_cast<const u32x4_t*>(qp + 32 * c);
       qf[c] = as_bf16x8(w);
     }
   }
 
   const float sl2 = rsqrtf((float)D) * 1.4426950408889634f;  // c = d^-1/2 * log2(e)
   float m = -INFINITY, l = 0.f;
-  f32x16_t o[NDB];
+  f32x4_t o[NDB];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
+  for (int b = 0; b < NDB; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Chunk loads: the stream's two waves split each chunk, the first half-wave
-  // pair loading the K rows and the second the v^T columns.
-  bf16_t* const sbuf = smem + str * 2 * STG;
-  const bf16_t* const gsrc =
-      qh == 0 ? a.k + (size_t)h * Rp * D : a.vt + (size_t)h * D * Rp;
-  const size_t cstride = qh == 0 ? (size_t)32 * D : (size_t)32;
+  // Chunk loads: waves 0-1 move the 32 K rows (16 U units each), waves 2-3
+  // the D v^T rows of 32 keys (2 D units each); lane-linear LDS slots, so the
+  // swizzle is applied to the global side.
+  const int part = wave >> 1, sub = wave & 1;
+  const bf16_t* const gsrc = part == 0 ? a.k + (size_t)h * Rp * D : a.vt + (size_t)h * D * Rp;
+  const size_t cstride = part == 0 ? (size_t)32 * D : (size_t)32;
   uint32_t goff[NDMA];  // byte offsets of this lane's 16-byte units within a chunk
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int p = i * 64 + lane;
-    if (qh == 0) {
+    const int p = sub * (NDMA * 64) + i * 64 + lane;  // LDS slot within the K (or v^T) chunk
+    if (part == 0) {
       const int row = p / U;
       goff[i] = 2u * (uint32_t)(row * D + (((p % U) ^ swz_k<D>(row)) * 8));
     } else {
@@ -219,7 +244,8 @@ void k_attn(AttnArgs a) {
       goff[i] = 2u * ((uint32_t)d * (uint32_t)a.Rp + (uint32_t)(((p & 3) ^ swz_v(d)) * 8));
     }
   }
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(sbuf + qh * CH));
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      lds_addr(ring + part * CH + sub * (NDMA * 64 * 8)));
   auto issue = [&](int stage, int chunk) {
     const uint64_t sa = (uint64_t)(uintptr_t)(gsrc + (size_t)chunk * cstride);
     // (the builtin returns int: widen through uint32_t, never by sign extension)
@@ -231,129 +257,100 @@ void k_attn(AttnArgs a) {
     for (int i = 0; i < NDMA; ++i) dma16(src, goff[i], dst + i * 1024);
   };
 
-  // Both streams run the same number of steps (a stream past the end of the
-  // list only takes part in the barriers).  Step j: wait for this wave's loads
-  // of chunk 2j + str, barrier (the partner wave's half has landed, and every
-  // wave is done with the other stage), start the loads of chunk 2j + 2 + str
-  // into the other stage, compute chunk 2j + str.
-  const int nstep = (nchunk + 1) >> 1;
+  // Step j: wait for this wave's loads of chunk j, barrier (every wave's part
+  // has landed, and every wave is done with the other stage), start the loads
+  // of chunk j + 1 into the other stage, compute chunk j.
   __builtin_amdgcn_s_waitcnt(0);  // q fragments in registers before the chunk stream starts
-  int chunk = str < nchunk ? chunk_at(str) : 0;
-  if (str < nchunk) issue(0, chunk);
-  for (int j = 0; j < nstep; ++j) {
-    const int ci = 2 * j + str, cur = j & 1;
+  int chunk = nchunk > 0 ? chunk_at(0) : 0;
+  if (nchunk > 0) issue(0, chunk);
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const int cur = ci & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int this_chunk = chunk;
-    if (ci + 2 < nchunk) {
-      chunk = chunk_at(ci + 2);
+    if (ci + 1 < nchunk) {
+      chunk = chunk_at(ci + 1);
       issue(cur ^ 1, chunk);
     }
-    // past the end of this stream's list, or no real query in this half (a
-    // block of at most 32 rows): only the loads and barriers above
-    if (ci >= nchunk || !q_live) continue;
+    if (!q_live) continue;  // no real query in this wave: loads and barriers only
     const int valid = sValid[this_chunk];
-    const bf16_t* kb = sbuf + cur * STG;
+    const bf16_t* kb = ring + cur * STG;
     const bf16_t* vb = kb + CH;
 
-    // S^T: K fragment (A operand, key l%32, d = 16c + 8g .. +7).
-    f32x16_t st;
+    // S^T, two 16-key blocks: K fragment (A operand, key 16 kk + l%16, d = 32 s + 8g .. +7).
+    f32x4_t st[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) st[e] = 0.f;
+    for (int kk = 0; kk < 2; ++kk) {
+      st[kk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int row = 16 * kk + l16;
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
-      const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-          kb + l32 * D + (((2 * c + g) ^ swz_k<D>(l32)) * 8)));
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st, 0, 0, 0);
+      for (int c = 0; c < NDS; ++c) {
+        const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
+            kb + row * D + (((4 * c + g) ^ swz_k<D>(row)) * 8)));
+        st[kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], st[kk], 0, 0, 0);
+      }
     }
 
     // Online softmax in the log2 domain: with c = d^-1/2 log2(e) and the
     // running max m of the raw scores, p = 2^(s c - m c); when some query's
     // max rises, its sum and accumulators are rescaled by 2^(m_old c - m c).
-    float sv[16];
+    float sv[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sv[e] = st[e];
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = st[0][e];
+      sv[4 + e] = st[1][e];
+    }
     if (valid < 32) {  // ragged chunk: rows at or beyond `valid` do not exist
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = 8 * (e >> 2) + 4 * g + (e & 3);
+      for (int e = 0; e < 8; ++e) {
+        const int key = 16 * (e >> 2) + 4 * g + (e & 3);
         sv[e] = key < valid ? sv[e] : -INFINITY;
       }
     }
     float mloc = sv[0];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[e]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, sv[e]);
+    mloc = max_x32(max_x16(mloc));
     const float m_new = fmaxf(m, mloc);
     if (__any(m_new > m)) {
       const float alpha = __builtin_amdgcn_exp2f((m - m_new) * sl2);  // 0 on the first chunk
       l *= alpha;
 #pragma unroll
-      for (int b = 0; b < NDB; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[b][e] *= alpha;
+      for (int b = 0; b < NDB; ++b) o[b] *= alpha;
       m = m_new;
     }
     const float mc = m * sl2;
-    float lsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -mc));
-      lsum += sv[e];
-    }
-    l += lsum;
-    const bf16x8_t p0 = pack8(sv), p1 = pack8(sv + 8);
+    for (int e = 0; e < 8; ++e) sv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -mc));
+    l += ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
+    const bf16x8_t p8 = pack8(sv);
 
-    // O^T += V^T P^T: V^T fragment (A operand, d row 32b + l%32, keys 16mm + 4g
-    // + {0..3, 8..11}).
+    // O^T += V^T P^T: V^T fragment (A operand, d row 16b + l%16, key slots 8g .. 8g+7).
 #pragma unroll
     for (int b = 0; b < NDB; ++b) {
-      const int d = 32 * b + l32;
-      const bf16x8_t v0 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-          vb + d * 32 + (((0 + g) ^ swz_v(d)) * 8)));
-      const bf16x8_t v1 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-          vb + d * 32 + (((2 + g) ^ swz_v(d)) * 8)));
-      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, p0, o[b], 0, 0, 0);
-      o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, p1, o[b], 0, 0, 0);
+      const int d = 16 * b + l16;
+      const bf16x8_t vf = as_bf16x8(
+          *reinterpret_cast<const u32x4_t*>(vb + d * 32 + ((g ^ swz_v(d)) * 8)));
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, p8, o[b], 0, 0, 0);
     }
   }
-  // each lane summed its own 16 keys of a chunk; the query's other 16 are in lane l ^ 32
-  l += __shfl_xor(l, 32, kWave);
+  // each lane summed its own 8 keys of a chunk; the query's other keys are in
+  // lanes l ^ 16, l ^ 32 and l ^ 48 (the same sum in every one of the four)
+  l = sum_x32(sum_x16(l));
 
-  // ---- combine the two streams: fixed order 0, 1 ----
-  __syncthreads();  // every wave is done with its chunk buffers (sO reuses them)
-  float (*sO)[D + 1] = reinterpret_cast<float (*)[D + 1]>(smem);
-  const int q = qh * 32 + l32;
-  if (g == 0) {
-    sM[str][q] = m;
-    sL[str][q] = l;
+  // ---- stage O / l (fp32) in LDS, row-major ----
+  __syncthreads();  // every wave is done with the ring (the staging reuses it)
+  float* const sO = reinterpret_cast<float*>(smem);
+  const int q = wave * 16 + l16;
+  if (q_live) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+      *reinterpret_cast<f32x4_t*>(&sO[q * SO + 16 * b + 4 * g]) = o[b] * inv;
   }
   __syncthreads();
-  const float M = fmaxf(sM[0][q], sM[1][q]);
-  const float f = m == -INFINITY ? 0.f : exp2f((m - M) * sl2);
-  if (str == 0 && g == 0) {
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 2; ++w)
-      L += sM[w][q] == -INFINITY ? 0.f : sL[w][q] * exp2f((sM[w][q] - M) * sl2);
-    sLt[q] = L;
-  }
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    if (str == w) {
-#pragma unroll
-      for (int b = 0; b < NDB; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int d = 32 * b + 8 * (e >> 2) + 4 * g + (e & 3);
-          const float val = o[b][e] * f;
-          sO[q][d] = (w == 0) ? val : sO[q][d] + val;
-        }
-    }
-    __syncthreads();
-  }
 
-  // ---- normalise, add the pooled branch, round, store row-major ----
+  // ---- add the pooled branch, round, store row-major ----
   const float* pooled = (!dense && a.pooled)
                             ? a.pooled + ((size_t)h * a.nQ + (tile - a.npt)) * D
                             : nullptr;
@@ -361,7 +358,6 @@ void k_attn(AttnArgs a) {
   for (int idx = tid; idx < 64 * (D / 8); idx += 256) {
     const int qq = idx / (D / 8), d8 = (idx % (D / 8)) * 8;
     if (qq >= nrows) continue;
-    const float inv = 1.0f / sLt[qq];
     u32x4_t gw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
     if (gated)
       gw = *reinterpret_cast<const u32x4_t*>(
@@ -369,7 +365,7 @@ void k_attn(AttnArgs a) {
     u32x4_t w;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      float x0 = sO[qq][d8 + 2 * t] * inv, x1 = sO[qq][d8 + 2 * t + 1] * inv;
+      float x0 = sO[qq * SO + d8 + 2 * t], x1 = sO[qq * SO + d8 + 2 * t + 1];
       if (pooled) {
         x0 = fmaf(bflo(gw[t]), pooled[d8 + 2 * t], x0);
         x1 = fmaf(bfhi(gw[t]), pooled[d8 + 2 * t + 1], x1);
@@ -386,8 +382,9 @@ bool attn_shape_ok(int n_chunks, int nsel) { return n_chunks <= kMaxChunks && ns
 
 hipError_t launch_attn(int head_dim, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.nqb * a.nh), block(256);
-  if (head_dim == 128) hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a);
+  const size_t dyn = sizeof(int) * (2 * (size_t)a.nsel + 1) + (size_t)a.n_chunks;
+  if (head_dim == 128) hipLaunchKernelGGL(k_attn<128>, grid, block, dyn, s, a);
+  else hipLaunchKernelGGL(k_attn<64>, grid, block, dyn, s, a);
   return hipGetLastError();
 }
 

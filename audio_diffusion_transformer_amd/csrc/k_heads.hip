@@ -15,8 +15,8 @@
 //   rope: (a, b) -> (a cos - b sin, b cos + a sin) on the pairs (i, i + D/2),
 //   cos/sin from the caller's table; the partner element sits D/16 lanes away.
 // v rows are staged in LDS and written transposed (v^T [nh][D][Rp]) in
-// 16-byte runs of 8 positions; within each aligned 16-row group the middle
-// two 4-row blocks are swapped (see below).  Padded rows (beyond a tile's
+// 16-byte runs of 8 positions; within each aligned 32-row group the 4-row
+// blocks are interleaved (see below).  Padded rows (beyond a tile's
 // length, up to the next multiple of 32) are written as zeros.  Tile sums of
 // q~, k~ and v are kept in fp32 per lane, combined across lanes and waves in
 // a fixed order, and divided by the tile's true row count.
@@ -158,16 +158,15 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
       }
     }
     // v^T: thread -> (dimension d, 8 positions).  Within every aligned group of
-    // 16 rows the 4-row blocks are stored in the order 0, 2, 1, 3, so that the
-    // 8 keys one lane feeds to the value-product MFMA (rows 4g..4g+3 and
-    // 8+4g..8+4g+3 of a 16-row group) are 16 contiguous bytes: positions
-    // 8h8 .. 8h8+7 of a group hold rows 4h8..4h8+3 and 8+4h8..8+4h8+3.
+    // 32 rows the 4-row blocks are stored in the order 0, 4, 1, 5, 2, 6, 3, 7,
+    // so that the 8 keys one lane feeds to the value-product MFMA (rows
+    // 4g..4g+3 and 16+4g..16+4g+3 of a 32-row chunk) are 16 contiguous bytes:
+    // positions 8p8 .. 8p8+7 hold rows 4p8..4p8+3 and 16+4p8..16+4p8+3.
 #pragma unroll
     for (int k2 = 0; k2 < D * 4 / 256; ++k2) {
       const int idx = k2 * 256 + tid;
       const int d = idx % D, p8 = idx / D;  // p8: 8-position run 0..3 of the 32-row group
-      const int g16 = p8 >> 1, h8 = p8 & 1;
-      const int r0 = 16 * g16 + 4 * h8, r1 = r0 + 8;
+      const int r0 = 4 * p8, r1 = r0 + 16;
       u32x4_t w;
       w[0] = (uint32_t)sV[(r0 + 0) * SV + d] | ((uint32_t)sV[(r0 + 1) * SV + d] << 16);
       w[1] = (uint32_t)sV[(r0 + 2) * SV + d] | ((uint32_t)sV[(r0 + 3) * SV + d] << 16);

@@ -15,11 +15,12 @@ def b2f(u):
 
 
 def vt_key_order(vt):
-    """v^T is stored with the middle two 4-row blocks of every 16-row group
-    swapped (an involution); undo it: [..., Rp] -> rows in order."""
+    """v^T stores the eight 4-row blocks of every 32-row group in the order
+    0, 4, 1, 5, 2, 6, 3, 7 (position 8p + 4h + e holds row 16h + 4p + e);
+    undo it: [..., Rp] -> rows in order."""
     sh = vt.shape
-    x = vt.reshape(sh[:-1] + (sh[-1] // 16, 4, 4))
-    return np.ascontiguousarray(x[..., [0, 2, 1, 3], :]).reshape(sh)
+    x = vt.reshape(sh[:-1] + (sh[-1] // 32, 4, 2, 4))
+    return np.ascontiguousarray(np.swapaxes(x, -3, -2)).reshape(sh)
 
 
 class BlockRun:
