@@ -88,12 +88,17 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "memory");
 }
 
-// XOR swizzle of the 16-byte units of a K row (D/8 units) and of a v^T row (4 units).
+// XOR swizzle of the 16-byte units of a K row (D/8 units) and of a v^T row (4
+// units).  ds_read_b128 is served 8 lanes at a time over 128 bytes (8 units):
+// the 8 consecutive K rows of such a group read one unit each, so their
+// swizzles must differ mod 8.
 template <int D>
 __device__ __forceinline__ int swz_k(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return D == 128 ? (row & 15) : (row & 7);
 }
-__device__ __forceinline__ int swz_v(int d) { return (d >> 2) & 3; }
+// (ds_read_b128 is served 8 lanes at a time over 128 bytes: the 8 v^T rows d
+// of one such group, 64 bytes apart, need distinct (d & 1, unit) pairs)
+__device__ __forceinline__ int swz_v(int d) { return (d >> 1) & 3; }
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_attn(AttnArgs a) {
