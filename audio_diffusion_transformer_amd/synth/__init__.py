@@ -267,6 +267,55 @@ def final_modulation(shape: Shape, step: int = 0, seed: int = SEED, amp=0.1):
     return uniform_f32(f"mod_final.step{step}", (3, 2, shape.hidden), -amp, amp, seed=seed)
 
 
+T_EMBED_DIM = 256  # width of the timestep frequency embedding (input of the time MLP)
+
+
+def rows_in_weights(shape: Shape, seed: int = SEED):
+    """F32 patch projections: w_video [H][c_video], w_audio [H][c_audio] ~
+    N(0, 1/c) (unit-variance rows from unit-variance patches), biases N(0, 0.02)."""
+    H, cv, ca = shape.hidden, shape.c_video, shape.c_audio
+    f = lambda name, shp, std: (normal_f64(name, shp, seed=seed) * std).astype(np.float32)
+    return {
+        "w_video": f("rows_in.w_video", (H, cv), cv ** -0.5),
+        "b_video": f("rows_in.b_video", (H,), 0.02),
+        "w_audio": f("rows_in.w_audio", (H, ca), ca ** -0.5),
+        "b_audio": f("rows_in.b_audio", (H,), 0.02),
+    }
+
+
+def time_weights(shape: Shape, n_blocks: int, seed: int = SEED, std: float = 0.02):
+    """Time MLP and modulation projections, bf16: w1 [H][256], w2 [H][H],
+    w_mod [6H][H], w_final [2H][H], their biases, and the per-block table
+    [n_blocks][6][H]."""
+    H = shape.hidden
+    shapes = {"w1": (H, T_EMBED_DIM), "b1": (H,), "w2": (H, H), "b2": (H,),
+              "w_mod": (6 * H, H), "b_mod": (6 * H,), "mod_table": (n_blocks, 6, H),
+              "w_final": (2 * H, H), "b_final": (2 * H,)}
+    return {k: normal_bf16("time." + k, shp, std, seed=seed) for k, shp in shapes.items()}
+
+
+def latents(shape: Shape, seed: int = SEED):
+    """Initial noise: video [V][c_video] and audio [A][c_audio] fp32 ~ N(0, 1)."""
+    return (normal_f64("latent.video", (shape.n_video, shape.c_video), seed=seed).astype(np.float32),
+            normal_f64("latent.audio", (shape.n_audio, shape.c_audio), seed=seed).astype(np.float32))
+
+
+def text_rows(shape: Shape, seed: int = SEED):
+    """Text-encoder rows of the prompt (stand-in): bf16 [T][H] ~ N(0, 1)."""
+    return normal_bf16("text_rows", (shape.n_text, shape.hidden), 1.0, seed=seed)
+
+
+def schedule(n_steps: int, shift: float = 5.0):
+    """Timesteps of n_steps denoising passes plus the terminal zero, fp32
+    [n_steps + 1][3] (text, audio, video): a linear grid 1 .. 1/n warped by
+    sigma' = shift sigma / (1 + (shift - 1) sigma), then 0; the three segments
+    share it (the caller may give each its own)."""
+    s = 1.0 - np.arange(n_steps, dtype=np.float64) / n_steps
+    s = shift * s / (1.0 + (shift - 1.0) * s)
+    s = np.concatenate([s, [0.0]])
+    return np.repeat(s[:, None], 3, axis=1).astype(np.float32)
+
+
 def lowrank_field(n_rows: int, rank: int = 4, seed: int = SEED, name="field"):
     """phi_j(p) = sin(2 pi f_j p / n + theta_j), f = (1, 3, 7, 17, ...): [n_rows][rank]."""
     freqs = np.asarray([1, 3, 7, 17, 31, 59][:rank], dtype=np.float64)

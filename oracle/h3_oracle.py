@@ -36,7 +36,13 @@ over video key tiles only; tile-mean divisor = true row count; pooled branch =
 softmax over all key tiles of the tile scores times the key tiles' value means,
 added in full precision before the bf16 rounding of the attention output; text
 and audio rows attend densely with no pooled term; softmax denominator uses the
-unrounded weights.
+unrounded weights.  For the denoising loop (the pages name its pieces, not
+their formulas): the rows in are F32 linear patch projections rounded once to
+bf16; the time embedder is a 256-wide cos/sin frequency embedding of
+t = 1000 sigma followed by Linear -> silu -> Linear; the modulation tables of
+a step are one shared projection of silu(c) per segment plus a per-block
+table, stored fp32; each pass ends with an Euler transition of the fp32
+latents on the caller's per-segment schedule.
 
 Parity against a released H3 / FastH3 checkpoint is unpinned (no weights,
 case file or reference velocities are available); every function here is
@@ -435,3 +441,105 @@ def routed_attn(sh, tile_start, n_prefix_tiles, q_bits, k_bits, v_bits, rows=Non
     g = None if gate is None else bf16_to_f64(gate)
     out = round_bf16(attention(q, k, v, ts, n_prefix_tiles, P, rt, bool(sh.pooled), rows, g))
     return dict(out=out, **rt)
+
+
+# ----------------------------------------------------------------------------
+# Rows in, time conditioning and the denoising loop
+# ----------------------------------------------------------------------------
+
+T_EMBED_DIM = 256        # width of the frequency embedding of the timestep
+T_SCALE = 1000.0         # timestep value t = T_SCALE * sigma
+T_MAX_PERIOD = 10000.0
+
+
+def rows_in(sh, text_bits, video_patch, audio_patch, w):
+    """The packed hidden stream from the rows: text rows as given (bf16), audio
+    and video patches through their F32 projections, F32 weights and inputs,
+    the sum rounded once to bf16 (h3.c README, implementation notes: the
+    96 -> 5376 video and 32 -> 5376 audio patch projections keep F32 weights,
+    inputs and accumulation and round the results straight into the packed
+    hidden stream; TensorFold PR #949, "What it adds": the rows in).
+
+    text_bits bf16 [T][H]; video_patch fp32 [V][cv]; audio_patch fp32 [A][ca];
+    w: w_video fp32 [H][cv], b_video [H], w_audio [H][ca], b_audio [H].
+    Returns float64 bf16 values [R][H] (text, audio, video)."""
+    f = lambda a: np.asarray(a, dtype=np.float32).astype(np.float64)
+    xv = round_bf16(linear(f(video_patch), f(w["w_video"]), f(w["b_video"])))
+    xa = round_bf16(linear(f(audio_patch), f(w["w_audio"]), f(w["b_audio"])))
+    xt = bf16_to_f64(np.asarray(text_bits, dtype=np.uint16)).reshape(sh.n_text, sh.hidden)
+    return np.concatenate([xt, xa, xv], axis=0)
+
+
+def timestep_embedding(t, dim=T_EMBED_DIM, max_period=T_MAX_PERIOD):
+    """Frequency embedding of a scalar timestep: [cos(t w_i)] ++ [sin(t w_i)],
+    w_i = max_period^(-i / (dim/2)), i < dim/2 (the pages name the time
+    embedder without its form; this is the usual diffusion-transformer one)."""
+    half = dim // 2
+    om = max_period ** (-np.arange(half, dtype=np.float64) / half)
+    a = float(t) * om
+    return np.concatenate([np.cos(a), np.sin(a)])
+
+
+def time_conditioning(sigma, tw):
+    """c = W2 silu(W1 e(T_SCALE sigma) + b1) + b2, [H], bf16 weights, carried
+    in float64 (TensorFold PR #949, "What comes next": the time embedder)."""
+    e = timestep_embedding(T_SCALE * float(sigma))
+    h1 = silu(linear(e[None, :], bf16_to_f64(tw["w1"]), bf16_to_f64(tw["b1"])))
+    return linear(h1, bf16_to_f64(tw["w2"]), bf16_to_f64(tw["b2"]))[0]
+
+
+def modulation_tables(sh, n_blocks, tw, sigma3):
+    """Modulation tables of one denoising step from the per-segment timesteps
+    sigma3 = (text, audio, video) (TensorFold PR #949, "What comes next": the
+    time embedder and modulation tables; h3.c README: video and audio follow
+    independent schedules).  For segment s with c_s = time_conditioning:
+      m_s        = W_mod silu(c_s) + b_mod                      [6H]
+      mod[l][s]  = m_s + table[l]                               [6][H]
+      final[s]   = W_final silu(c_s) + b_final                  [2][H]
+    stored as fp32 (the tables' storage type).  Returns (mod [L][3][6][H],
+    mod_final [3][2][H]) as float64 values of fp32 numbers."""
+    H = sh.hidden
+    wm, bm = bf16_to_f64(tw["w_mod"]), bf16_to_f64(tw["b_mod"])
+    wf, bfin = bf16_to_f64(tw["w_final"]), bf16_to_f64(tw["b_final"])
+    table = bf16_to_f64(tw["mod_table"]).reshape(n_blocks, 6, H)
+    mod = np.empty((n_blocks, 3, 6, H))
+    fin = np.empty((3, 2, H))
+    for s in range(3):
+        a = silu(time_conditioning(sigma3[s], tw))[None, :]
+        m = linear(a, wm, bm)[0].reshape(6, H)
+        mod[:, s] = m[None] + table
+        fin[s] = linear(a, wf, bfin)[0].reshape(2, H)
+    return round_f32(mod), round_f32(fin)
+
+
+def euler_step(latent, vel, sigma_from, sigma_to):
+    """One Euler transition of the flow ODE, x <- x + (sigma_to - sigma_from) v,
+    on fp32 latents (h3.c README: the sampler's Euler transitions, video and
+    audio on their own schedules, a terminal zero after the last pass)."""
+    x = np.asarray(latent, dtype=np.float32).astype(np.float64)
+    return round_f32(x + (float(np.float32(sigma_to)) - float(np.float32(sigma_from))) *
+                     np.asarray(vel, dtype=np.float64))
+
+
+def denoise(sh, tile_start, n_prefix_tiles, blocks, head, rows_w, tw, sigmas, rope, text_bits,
+            video_latent, audio_latent):
+    """The denoising loop: for every pass k, the rows in from the current
+    latents, the modulation tables from the timesteps sigmas[k] = (text,
+    audio, video), the L-block forward and heads, then one Euler transition of
+    the video and audio latents to sigmas[k + 1] (the caller's schedule; its
+    last entry is the terminal zero).  Returns the final latents (fp32 values)
+    and the velocities of every pass."""
+    lat_v = np.asarray(video_latent, dtype=np.float32).astype(np.float64)
+    lat_a = np.asarray(audio_latent, dtype=np.float32).astype(np.float64)
+    sig = np.asarray(sigmas, dtype=np.float32)
+    L = len(blocks)
+    vels = []
+    for k in range(len(sig) - 1):
+        x = rows_in(sh, text_bits, lat_v, lat_a, rows_w)
+        mod, fin = modulation_tables(sh, L, tw, sig[k])
+        r = dit_forward(sh, tile_start, n_prefix_tiles, blocks, head, mod, fin, rope,
+                        f64_to_bf16_bits(x))
+        vels.append((r["vel_video"], r["vel_audio"]))
+        lat_v = euler_step(lat_v, r["vel_video"], sig[k][2], sig[k + 1][2])
+        lat_a = euler_step(lat_a, r["vel_audio"], sig[k][1], sig[k + 1][1])
+    return dict(video=lat_v, audio=lat_a, vels=vels)

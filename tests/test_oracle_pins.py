@@ -555,3 +555,136 @@ def test_cube_tiles_cover_the_grid():
         t, h, w = p // (Hh * W), (p // W) % Hh, p % W
         assert t.max() - t.min() < 4 and h.max() - h.min() < 4 and w.max() - w.min() < 4
         assert len(p) == (t.max() - t.min() + 1) * (h.max() - h.min() + 1) * (w.max() - w.min() + 1)
+
+
+# ----------------------------------------------------------------------------
+# Rows in, time conditioning, modulation tables, the Euler loop
+# ----------------------------------------------------------------------------
+
+def test_timestep_embedding_closed_forms():
+    e0 = O.timestep_embedding(0.0)
+    np.testing.assert_array_equal(e0, np.r_[np.ones(128), np.zeros(128)])
+    e = O.timestep_embedding(100.0 * math.pi)
+    # w_0 = 1 and w_64 = 10000^(-1/2) = 1/100: cos(100 pi) = 1, cos(pi) = -1
+    assert abs(e[0] - 1.0) < 1e-12 and abs(e[128]) < 1e-12
+    assert abs(e[64] + 1.0) < 1e-12 and abs(e[128 + 64]) < 1e-12
+    assert abs(e[127] - math.cos(100.0 * math.pi * 10000.0 ** (-127 / 128))) < 1e-12
+
+
+def _time_w(H=2, L=1):
+    z = lambda *s: np.zeros(s)
+    tw = {"w1": z(H, 256), "b1": z(H), "w2": z(H, H), "b2": z(H), "w_mod": z(6 * H, H),
+          "b_mod": z(6 * H), "mod_table": z(L, 6, H), "w_final": z(2 * H, H), "b_final": z(2 * H)}
+    return tw
+
+
+def test_time_conditioning_hand_example():
+    tw = _time_w()
+    tw["w1"][0, 0] = 1.0          # (W1 e)_0 = e_0 = cos(t)
+    tw["w1"][1, 0] = -1.0         # (W1 e)_1 = -cos(t)
+    tw["w2"][:] = [[0.0, 1.0], [2.0, 0.0]]
+    tw["b2"][:] = [0.5, 0.0]
+    tb = {k: bits(v) for k, v in tw.items()}
+    s1, sm1 = 0.7310585786300049, -0.2689414213699951   # silu(1) = logistic(1), silu(-1)
+    c = O.time_conditioning(0.0, tb)                     # t = 0: e_0 = 1
+    np.testing.assert_allclose(c, [sm1 + 0.5, 2 * s1], rtol=1e-14)
+    c = O.time_conditioning(math.pi / O.T_SCALE, tb)     # t = pi: e_0 = -1
+    np.testing.assert_allclose(c, [s1 + 0.5, 2 * sm1], rtol=1e-6)
+
+
+def test_modulation_tables_layout_and_segments():
+    H, L = 2, 3
+    tw = _time_w(H, L)
+    tw["b_mod"][:] = np.arange(6 * H) * 0.125            # entry j*H + c -> mod[.][.][j][c]
+    tw["mod_table"][:] = np.arange(L)[:, None, None] * 4.0
+    tw["b_final"][:] = -np.arange(2 * H) * 0.5
+    tw["w1"][0, 0] = 1.0
+    tw["w2"][0, 0] = 1.0
+    tw["w_mod"][:, 0] = 0.25                             # m depends on the segment's timestep
+    tb = {k: bits(v) for k, v in tw.items()}
+    sh = Sh(1, 1, 1, 1, 2, 1)
+    sh.hidden = H
+    mod, fin = O.modulation_tables(sh, L, tb, np.array([0.0, 0.5, math.pi / O.T_SCALE]))
+    assert mod.shape == (L, 3, 6, H) and fin.shape == (3, 2, H)
+    # segment 0 (t = 0): c_0 = silu(1); m = 0.25 silu(c_0) + b_mod
+    m0 = 0.25 * float(O.silu(np.array([0.7310585786300049]))[0])
+    for l in range(L):
+        for j in range(6):
+            for c in range(H):
+                assert abs(mod[l, 0, j, c] - (m0 + 0.125 * (j * H + c) + 4.0 * l)) < 1e-5
+    np.testing.assert_array_equal(fin[:, 0, 1], [-0.5] * 3)
+    np.testing.assert_array_equal(fin[:, 1, 1], [-1.5] * 3)
+    # the block table shifts every segment alike; the segments differ by their timesteps
+    # (each entry is an fp32 value: m + 8 and m round at different spacings)
+    np.testing.assert_allclose(mod[2] - mod[0], np.full((3, 6, H), 8.0), atol=2 ** -19)
+    assert np.all(mod[0, 0] != mod[0, 2])
+
+
+def test_rows_in_identity_projection_and_segment_order():
+    sh = Sh(2, 3, 4, 1, 4, 1)
+    sh.hidden, sh.c_video, sh.c_audio = 128, 96, 32
+    H = sh.hidden
+    text = bits(np.full((2, H), 3.0))
+    pv = (np.arange(4 * 96).reshape(4, 96) % 7 - 3).astype(np.float32) * 0.5
+    pa = (np.arange(3 * 32).reshape(3, 32) % 5).astype(np.float32)
+    w = {"w_video": np.eye(H, 96, dtype=np.float32), "b_video": np.full(H, 0.25, np.float32),
+         "w_audio": 2 * np.eye(H, 32, dtype=np.float32), "b_audio": np.full(H, -1.0, np.float32)}
+    x = O.rows_in(sh, text, pv, pa, w)
+    np.testing.assert_array_equal(x[:2], 3.0)
+    np.testing.assert_array_equal(x[2:5, :32], 2 * pa - 1.0)
+    np.testing.assert_array_equal(x[2:5, 32:], -1.0)
+    np.testing.assert_array_equal(x[5:, :96], pv + 0.25)
+    np.testing.assert_array_equal(x[5:, 96:], 0.25)
+
+
+def test_rows_in_keeps_f32_weights():
+    """A weight 1 + 2^-10 is not a bf16 value: 64 products of it accumulate to
+    64 + 2^-4, which rounds to bf16 65.0 only if the weight was not rounded."""
+    sh = Sh(0, 0, 1, 1, 4, 1)
+    sh.hidden, sh.c_video, sh.c_audio = 1, 64, 1
+    w = {"w_video": np.full((1, 64), 1 + 2 ** -10, np.float32), "b_video": np.full(1, 0.5 - 2 ** -5, np.float32),
+         "w_audio": np.zeros((1, 1), np.float32), "b_audio": np.zeros(1, np.float32)}
+    x = O.rows_in(sh, np.zeros((0, 1), np.uint16), np.ones((1, 64), np.float32),
+                  np.zeros((0, 1), np.float32), w)
+    # 64 + 1/16 + 1/2 - 1/32 = 64.53125 -> bf16 spacing at 64 is 0.5 -> 64.5
+    assert x[0, 0] == 64.5
+
+
+def test_euler_constant_velocity_closed_form():
+    lat = np.array([[1.0, -2.0], [0.5, 3.0]], np.float32)
+    v = np.array([[0.25, 1.0], [-2.0, 0.5]])
+    x = lat
+    for s0, s1 in zip([1.0, 0.5, 0.25], [0.5, 0.25, 0.0]):
+        x = O.euler_step(x, v, s0, s1)
+    np.testing.assert_array_equal(x, lat - v)
+
+
+def test_denoise_with_constant_heads_follows_the_schedules():
+    """With zero head weights the velocities are the head biases whatever the
+    blocks compute, so the loop must land on x0 + (sigma_end - sigma_0) b, per
+    segment on its own schedule column (text, audio, video)."""
+    from audio_diffusion_transformer_amd import synth as S
+    sh = S.TINY.replace(n_text=64, n_audio=64, n_video=128)
+    ts, npt = S.tile_map(sh)
+    blocks = [S.block_weights(sh, block=0)]
+    head = S.head_weights(sh)
+    head["w_video"] = np.zeros_like(head["w_video"])
+    head["w_audio"] = np.zeros_like(head["w_audio"])
+    head["b_video"] = bits(np.full(sh.c_video, 0.5))
+    head["b_audio"] = bits(np.full(sh.c_audio, -0.25))
+    sig = np.array([[1.0, 1.0, 1.0], [0.5, 0.75, 0.5], [0.25, 0.5, 0.25], [0.0, 0.25, 0.0]],
+                   np.float32)
+    lv, la = S.latents(sh)
+    r = O.denoise(sh, ts, npt, blocks, head, S.rows_in_weights(sh), S.time_weights(sh, 1), sig,
+                  S.rope_tables(sh), S.text_rows(sh), lv, la)
+    # the same transitions in IEEE float32 arithmetic (each step's sum rounds
+    # once; the steps (sigma_to - sigma_from) * b are exact dyadic values)
+    ev, ea = lv.copy(), la.copy()
+    for k in range(3):
+        ev = ev + np.float32((sig[k + 1, 2] - sig[k, 2]) * 0.5)
+        ea = ea + np.float32((sig[k + 1, 1] - sig[k, 1]) * -0.25)
+    np.testing.assert_array_equal(r["video"], ev.astype(np.float64))
+    np.testing.assert_array_equal(r["audio"], ea.astype(np.float64))
+    np.testing.assert_allclose(r["video"], lv - 0.5, atol=1e-6)
+    np.testing.assert_allclose(r["audio"], la + 0.25 * 0.75, atol=1e-6)
+    assert len(r["vels"]) == 3
