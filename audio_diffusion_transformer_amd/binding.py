@@ -17,10 +17,10 @@ LIB_PATH = os.path.join(_HERE, "libh3.so")
 
 H3_OK, H3_EINVAL, H3_EWORKSPACE, H3_EHIP, H3_EUNSUPPORTED = 0, -1, -2, -3, -4
 H3_WS_BLOCK, H3_WS_DIT, H3_WS_ATTN = 0, 1, 2
-ABI_VERSION = 2  # must match H3_ABI_VERSION in include/h3.h
+ABI_VERSION = 3  # must match H3_ABI_VERSION in include/h3.h
 
 KERNEL_CLASSES = ["modnorm", "gemm_qkv", "heads", "route", "attn", "gemm_o", "gemm_fc1",
-                  "gemm_fc2", "final", "tables"]
+                  "gemm_fc2", "final", "tables", "rows_in", "time", "euler"]
 
 _vp = ctypes.c_void_p
 
@@ -43,6 +43,16 @@ class H3BlockWeights(ctypes.Structure):
 class H3HeadWeights(ctypes.Structure):
     _fields_ = [("w_video", _vp), ("b_video", _vp), ("w_audio", _vp), ("b_audio", _vp),
                 ("c_video", ctypes.c_int32), ("c_audio", ctypes.c_int32)]
+
+
+class H3RowsInWeights(ctypes.Structure):
+    _fields_ = [("w_video", _vp), ("b_video", _vp), ("w_audio", _vp), ("b_audio", _vp),
+                ("c_video", ctypes.c_int32), ("c_audio", ctypes.c_int32)]
+
+
+class H3TimeWeights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w1", "b1", "w2", "b2", "w_mod", "b_mod", "mod_table",
+                                   "w_final", "b_final")]
 
 
 class H3WsLayout(ctypes.Structure):
@@ -84,13 +94,27 @@ def lib():
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.h3_routed_attn.argtypes = [ctypes.POINTER(H3Shape), i32p, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, ctypes.c_size_t, _vp]
+    L.h3_rows_in.argtypes = [ctypes.POINTER(H3Shape), ctypes.POINTER(H3RowsInWeights), _vp,
+                             _vp, _vp, _vp, _vp]
+    L.h3_modulation_workspace_bytes.argtypes = [ctypes.POINTER(H3Shape)]
+    L.h3_modulation_workspace_bytes.restype = ctypes.c_size_t
+    f32p = ctypes.POINTER(ctypes.c_float)
+    L.h3_modulation.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32,
+                                ctypes.POINTER(H3TimeWeights), f32p, _vp, _vp, _vp,
+                                ctypes.c_size_t, _vp]
+    L.h3_denoise_workspace_bytes.argtypes = [ctypes.POINTER(H3Shape), i32p, ctypes.c_int32]
+    L.h3_denoise_workspace_bytes.restype = ctypes.c_size_t
+    L.h3_denoise.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32, ctypes.c_int32, i32p,
+                             ctypes.POINTER(H3BlockWeights), ctypes.POINTER(H3HeadWeights),
+                             ctypes.POINTER(H3RowsInWeights), ctypes.POINTER(H3TimeWeights),
+                             f32p, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.h3_prof_enable.argtypes = [ctypes.c_int]
     L.h3_prof_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                ctypes.POINTER(ctypes.c_double)]
     L.h3_prof_kernel_name.argtypes = [ctypes.c_int32]
     L.h3_prof_kernel_name.restype = ctypes.c_char_p
     for f in (L.h3_workspace_layout, L.h3_block_forward, L.h3_dit_forward, L.h3_routed_attn,
-              L.h3_prof_enable, L.h3_prof_read):
+              L.h3_rows_in, L.h3_modulation, L.h3_denoise, L.h3_prof_enable, L.h3_prof_read):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -184,6 +208,71 @@ def routed_attn(shape, tile_start, q, k, v, out, ws, sel=None, scores=None, gate
     _check(lib().h3_routed_attn(ctypes.byref(shape), tp, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                                 _ptr(out), _ptr(sel), _ptr(scores), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def rows_in_weights_struct(w):
+    """w: dict of device fp32 tensors w_video [H][cv], b_video, w_audio [H][ca], b_audio."""
+    return H3RowsInWeights(_ptr(w["w_video"]), _ptr(w["b_video"]), _ptr(w["w_audio"]),
+                           _ptr(w["b_audio"]), int(w["w_video"].shape[1]),
+                           int(w["w_audio"].shape[1]))
+
+
+def time_weights_struct(tw):
+    return H3TimeWeights(*[_ptr(tw[n]) for n, _ in H3TimeWeights._fields_])
+
+
+def _f32_host(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def rows_in(shape, w, text_rows, audio_patch, video_patch, x, stream=None):
+    ws_ = rows_in_weights_struct(w) if isinstance(w, dict) else w
+    _check(lib().h3_rows_in(ctypes.byref(shape), ctypes.byref(ws_), _ptr(text_rows),
+                            _ptr(audio_patch), _ptr(video_patch), _ptr(x), _stream(stream)))
+
+
+def modulation_workspace_bytes(shape):
+    n = lib().h3_modulation_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise H3Error(H3_EINVAL, last_error())
+    return n
+
+
+def modulation(shape, n_blocks, tw, sigma3, mod, mod_final, ws, stream=None):
+    """sigma3: host (text, audio, video) timesteps."""
+    tws = time_weights_struct(tw) if isinstance(tw, dict) else tw
+    sg, sp = _f32_host(sigma3)
+    _check(lib().h3_modulation(ctypes.byref(shape), n_blocks, ctypes.byref(tws), sp, _ptr(mod),
+                               _ptr(mod_final), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream)))
+
+
+def denoise_workspace_bytes(shape, tile_start, n_blocks):
+    ts, tp = _tiles(tile_start)
+    n = lib().h3_denoise_workspace_bytes(ctypes.byref(shape), tp, n_blocks)
+    if n == 0:
+        raise H3Error(H3_EINVAL, last_error())
+    return n
+
+
+def denoise(shape, tile_start, blocks, heads, rows_w, tw, sigmas, rope, text_rows, video_latent,
+            audio_latent, ws, stream=None):
+    """sigmas: host [n_steps + 1][3]; the latents (fp32 device) are updated in place."""
+    ts, tp = _tiles(tile_start)
+    if isinstance(blocks, (list, tuple)):
+        arr = (H3BlockWeights * max(len(blocks), 1))(*[block_weights_struct(b) for b in blocks])
+        n = len(blocks)
+    else:
+        arr, n = blocks, len(blocks)
+    hw = head_weights_struct(heads) if isinstance(heads, dict) else heads
+    rw = rows_in_weights_struct(rows_w) if isinstance(rows_w, dict) else rows_w
+    tws = time_weights_struct(tw) if isinstance(tw, dict) else tw
+    sg, sp = _f32_host(sigmas)
+    _check(lib().h3_denoise(ctypes.byref(shape), n, len(sg) - 1, tp, arr, ctypes.byref(hw),
+                            ctypes.byref(rw), ctypes.byref(tws), sp, _ptr(rope), _ptr(text_rows),
+                            _ptr(video_latent), _ptr(audio_latent), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def prof_enable(on=True):

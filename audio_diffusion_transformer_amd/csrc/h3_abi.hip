@@ -374,6 +374,150 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
   return H3_OK;
 }
 
+int check_dit_args(const Plan& p, int n_blocks, const h3_block_weights* blocks,
+                   const h3_head_weights* heads) {
+  int rc;
+  if (n_blocks < 0) return fail(H3_EINVAL, "n_blocks < 0");
+  if (n_blocks > 0 && !blocks) return fail(H3_EINVAL, "blocks is NULL");
+  for (int l = 0; l < n_blocks; ++l)
+    if ((rc = check_block_weights(&blocks[l], l))) return rc;
+  if (!heads || !heads->w_video || !heads->b_video || !heads->w_audio || !heads->b_audio)
+    return fail(H3_EINVAL, "head weights are required");
+  if (heads->c_video < 1 || heads->c_video > 256 || heads->c_audio < 1 || heads->c_audio > 256)
+    return fail(H3_EINVAL, "head widths must be in [1, 256]");
+  if (!aligned16(heads->w_video) || !aligned16(heads->w_audio))
+    return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
+  (void)p;
+  return H3_OK;
+}
+
+// L blocks, then the final modulated norm of the audio and video rows and the heads.
+int run_dit(const Plan& p, void* ws, int n_blocks, const h3_block_weights* blocks,
+            const h3_head_weights* heads, const float* mod, const float* mod_final,
+            const float* rope, const bf16_t* x_in, float* vel_video, float* vel_audio,
+            hipStream_t st) {
+  int rc;
+  const bf16_t* x = x_in;
+  bf16_t* xa = at<bf16_t>(ws, p.lay.xa);
+  bf16_t* xb = at<bf16_t>(ws, p.lay.xb);
+  const size_t mstride = (size_t)3 * 6 * p.H;
+  for (int l = 0; l < n_blocks; ++l) {
+    bf16_t* xo = (l & 1) ? xb : xa;
+    if ((rc = run_block(p, ws, &blocks[l], mod + l * mstride, rope, x, xo, st))) return rc;
+    x = xo;
+  }
+  bf16_t* z = at<bf16_t>(ws, p.lay.norm);
+  const int H = p.H, nt = p.s.n_text;
+  prof_begin(H3_K_FINAL, st);
+  H3_TRY(launch_modnorm(x, z, nt, mod_final + 0 * H, mod_final + 1 * H, 2 * H, nt, p.R, H, nt,
+                        p.P, p.s.norm_eps, st));
+  H3_TRY(launch_out_head(z, p.s.n_audio, H, heads->w_audio, heads->b_audio, heads->c_audio,
+                         vel_audio, st));
+  H3_TRY(launch_out_head(z + (size_t)p.s.n_audio * H, p.s.n_video, H, heads->w_video,
+                         heads->b_video, heads->c_video, vel_video, st));
+  prof_end(H3_K_FINAL, st);
+  return H3_OK;
+}
+
+int check_rows_in(const h3_shape* s, const h3_rows_in_weights* w, const h3_bf16* text,
+                  const float* audio, const float* video, const h3_bf16* x) {
+  if (!s) return fail(H3_EINVAL, "shape is NULL");
+  if (s->n_text < 0 || s->n_audio < 0 || s->n_video < 0) return fail(H3_EINVAL, "negative row count");
+  if (s->hidden < 256 || s->hidden % 256 != 0 || s->hidden > 8192)
+    return fail(H3_EUNSUPPORTED, "hidden %d must be a positive multiple of 256, <= 8192", s->hidden);
+  if (!w) return fail(H3_EINVAL, "rows-in weights are required");
+  if (w->c_video < 1 || w->c_video > 256 || w->c_audio < 1 || w->c_audio > 256)
+    return fail(H3_EINVAL, "patch widths must be in [1, 256]");
+  if ((s->n_video > 0 && (!video || !w->w_video || !w->b_video)) ||
+      (s->n_audio > 0 && (!audio || !w->w_audio || !w->b_audio)) || (s->n_text > 0 && !text) || !x)
+    return fail(H3_EINVAL, "rows-in inputs, weights and x are required");
+  if ((text && !aligned16(text)) || !aligned16(x) || (w->b_video && !aligned16(w->b_video)) ||
+      (w->b_audio && !aligned16(w->b_audio)))
+    return fail(H3_EINVAL, "text rows, x and the biases must be 16-byte aligned");
+  return H3_OK;
+}
+
+int run_rows_in(const h3_shape& s, const h3_rows_in_weights* w, const h3_bf16* text,
+                const float* audio, const float* video, bf16_t* x, hipStream_t st) {
+  RowsInArgs a{};
+  a.text = text;
+  a.audio = audio;
+  a.video = video;
+  a.w_audio = w->w_audio;
+  a.b_audio = w->b_audio;
+  a.w_video = w->w_video;
+  a.b_video = w->b_video;
+  a.x = x;
+  a.n_text = s.n_text;
+  a.n_audio = s.n_audio;
+  a.n_video = s.n_video;
+  a.H = s.hidden;
+  a.c_audio = w->c_audio;
+  a.c_video = w->c_video;
+  prof_begin(H3_K_ROWS_IN, st);
+  H3_TRY(launch_rows_in(a, st));
+  prof_end(H3_K_ROWS_IN, st);
+  return H3_OK;
+}
+
+int check_time_weights(const h3_time_weights* tw, int n_blocks) {
+  if (!tw || !tw->w1 || !tw->b1 || !tw->w2 || !tw->b2 || !tw->w_final || !tw->b_final ||
+      (n_blocks > 0 && (!tw->w_mod || !tw->b_mod || !tw->mod_table)))
+    return fail(H3_EINVAL, "time weights are required");
+  if (!aligned16(tw->w1) || !aligned16(tw->w2) || !aligned16(tw->w_final) ||
+      (tw->w_mod && !aligned16(tw->w_mod)))
+    return fail(H3_EINVAL, "time weight matrices must be 16-byte aligned");
+  return H3_OK;
+}
+
+// scratch: 6H floats (h [3][H], then c [3][H])
+int run_modulation(int H, int n_blocks, const h3_time_weights* tw, const float* sigma3,
+                   float* mod, float* mod_final, float* scratch, hipStream_t st) {
+  float* h = scratch;
+  float* c = scratch + 3 * H;
+  TimeGemvArgs a{};
+  for (int i = 0; i < 3; ++i) a.sigma[i] = sigma3[i];
+  prof_begin(H3_K_TIME, st);
+  a.in = nullptr; a.w = tw->w1; a.b = tw->b1; a.table = nullptr; a.out = h;
+  a.K = kTimeEmbedDim; a.N = H; a.n_blocks = 0; a.in_silu = 0; a.out_silu = 1;
+  H3_TRY(launch_time_gemv(a, st));
+  a.in = h; a.w = tw->w2; a.b = tw->b2; a.out = c; a.K = H; a.N = H; a.out_silu = 0;
+  H3_TRY(launch_time_gemv(a, st));
+  if (n_blocks > 0) {
+    a.in = c; a.in_silu = 1; a.w = tw->w_mod; a.b = tw->b_mod; a.table = tw->mod_table;
+    a.out = mod; a.N = 6 * H; a.n_blocks = n_blocks;
+    H3_TRY(launch_time_gemv(a, st));
+  }
+  a.in = c; a.in_silu = 1; a.w = tw->w_final; a.b = tw->b_final; a.table = nullptr;
+  a.out = mod_final; a.N = 2 * H; a.n_blocks = 0;
+  H3_TRY(launch_time_gemv(a, st));
+  prof_end(H3_K_TIME, st);
+  return H3_OK;
+}
+
+struct DenoiseLayout {
+  size_t x, mod, mod_final, vel_video, vel_audio, time, total;
+};
+
+// the forward's workspace, then the denoising loop's own buffers
+DenoiseLayout denoise_layout(const Plan& p, int n_blocks) {
+  DenoiseLayout d{};
+  size_t off = p.lay.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  d.x = take((size_t)p.R * p.H * 2);
+  d.mod = take((size_t)(n_blocks > 0 ? n_blocks : 1) * 3 * 6 * p.H * 4);
+  d.mod_final = take((size_t)3 * 2 * p.H * 4);
+  d.vel_video = take((size_t)(p.s.n_video > 0 ? p.s.n_video : 1) * 256 * 4);
+  d.vel_audio = take((size_t)(p.s.n_audio > 0 ? p.s.n_audio : 1) * 256 * 4);
+  d.time = take((size_t)6 * p.H * 4);
+  d.total = off;
+  return d;
+}
+
 // ---------------------------------------------------------------------------
 // Kernel-time accounting
 // ---------------------------------------------------------------------------
@@ -469,43 +613,106 @@ int h3_dit_forward(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_
   int rc = make_plan(shape, tile_start, H3_WS_DIT, p);
   if (rc) return rc;
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
-  if (n_blocks < 0) return fail(H3_EINVAL, "n_blocks < 0");
-  if (n_blocks > 0 && !blocks) return fail(H3_EINVAL, "blocks is NULL");
-  for (int l = 0; l < n_blocks; ++l)
-    if ((rc = check_block_weights(&blocks[l], l))) return rc;
-  if (!heads || !heads->w_video || !heads->b_video || !heads->w_audio || !heads->b_audio)
-    return fail(H3_EINVAL, "head weights are required");
-  if (heads->c_video < 1 || heads->c_video > 256 || heads->c_audio < 1 || heads->c_audio > 256)
-    return fail(H3_EINVAL, "head widths must be in [1, 256]");
+  if ((rc = check_dit_args(p, n_blocks, blocks, heads))) return rc;
   if ((n_blocks > 0 && !mod) || !mod_final || !x_in)
     return fail(H3_EINVAL, "mod, mod_final and x_in are required");
   if ((p.s.n_video > 0 && !vel_video) || (p.s.n_audio > 0 && !vel_audio))
     return fail(H3_EINVAL, "velocity outputs are required");
   if (!aligned16(x_in) || (mod && !aligned16(mod)) || !aligned16(mod_final) ||
-      (rope && !aligned16(rope)) || !aligned16(heads->w_video) || !aligned16(heads->w_audio))
+      (rope && !aligned16(rope)))
     return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   if ((rc = upload_tables(p, ws, st))) return rc;
-  const bf16_t* x = x_in;
-  bf16_t* xa = at<bf16_t>(ws, p.lay.xa);
-  bf16_t* xb = at<bf16_t>(ws, p.lay.xb);
-  const size_t mstride = (size_t)3 * 6 * p.H;
-  for (int l = 0; l < n_blocks; ++l) {
-    bf16_t* xo = (l & 1) ? xb : xa;
-    if ((rc = run_block(p, ws, &blocks[l], mod + l * mstride, rope, x, xo, st))) return rc;
-    x = xo;
+  return run_dit(p, ws, n_blocks, blocks, heads, mod, mod_final, rope, x_in, vel_video,
+                 vel_audio, st);
+}
+
+size_t h3_modulation_workspace_bytes(const h3_shape* shape) {
+  if (!shape || shape->hidden < 256 || shape->hidden % 256 != 0 || shape->hidden > 8192) {
+    fail(H3_EINVAL, "hidden must be a positive multiple of 256, at most 8192");
+    return 0;
   }
-  // final modulated norm of the audio and video rows, then the heads
-  bf16_t* z = at<bf16_t>(ws, p.lay.norm);
-  const int H = p.H, nt = p.s.n_text;
-  prof_begin(H3_K_FINAL, st);
-  H3_TRY(launch_modnorm(x, z, nt, mod_final + 0 * H, mod_final + 1 * H, 2 * H, nt, p.R, H, nt,
-                        p.P, p.s.norm_eps, st));
-  H3_TRY(launch_out_head(z, p.s.n_audio, H, heads->w_audio, heads->b_audio, heads->c_audio,
-                         vel_audio, st));
-  H3_TRY(launch_out_head(z + (size_t)p.s.n_audio * H, p.s.n_video, H, heads->w_video,
-                         heads->b_video, heads->c_video, vel_video, st));
-  prof_end(H3_K_FINAL, st);
+  return align256((size_t)6 * shape->hidden * sizeof(float));
+}
+
+int h3_modulation(const h3_shape* shape, int32_t n_blocks, const h3_time_weights* tw,
+                  const float* sigma3, float* mod, float* mod_final, void* ws, size_t ws_bytes,
+                  void* stream) {
+  const size_t need = h3_modulation_workspace_bytes(shape);
+  if (need == 0) return H3_EINVAL;
+  if (n_blocks < 0) return fail(H3_EINVAL, "n_blocks < 0");
+  if (!sigma3) return fail(H3_EINVAL, "sigma3 is NULL");
+  int rc;
+  if ((rc = check_time_weights(tw, n_blocks))) return rc;
+  if ((n_blocks > 0 && !mod) || !mod_final) return fail(H3_EINVAL, "mod and mod_final are required");
+  if (!ws || ((uintptr_t)ws & 255) != 0) return fail(H3_EINVAL, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(H3_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  return run_modulation(shape->hidden, n_blocks, tw, sigma3, mod, mod_final,
+                        static_cast<float*>(ws), (hipStream_t)stream);
+}
+
+int h3_rows_in(const h3_shape* shape, const h3_rows_in_weights* w, const h3_bf16* text_rows,
+               const float* audio_patch, const float* video_patch, h3_bf16* x, void* stream) {
+  int rc;
+  if ((rc = check_rows_in(shape, w, text_rows, audio_patch, video_patch, x))) return rc;
+  return run_rows_in(*shape, w, text_rows, audio_patch, video_patch, x, (hipStream_t)stream);
+}
+
+size_t h3_denoise_workspace_bytes(const h3_shape* shape, const int32_t* tile_start,
+                                  int32_t n_blocks) {
+  Plan p;
+  if (make_plan(shape, tile_start, H3_WS_DIT, p) != H3_OK) return 0;
+  if (n_blocks < 0) {
+    fail(H3_EINVAL, "n_blocks < 0");
+    return 0;
+  }
+  return denoise_layout(p, n_blocks).total;
+}
+
+int h3_denoise(const h3_shape* shape, int32_t n_blocks, int32_t n_steps,
+               const int32_t* tile_start, const h3_block_weights* blocks,
+               const h3_head_weights* heads, const h3_rows_in_weights* rows_w,
+               const h3_time_weights* tw, const float* sigmas, const float* rope,
+               const h3_bf16* text_rows, float* video_latent, float* audio_latent, void* ws,
+               size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, tile_start, H3_WS_DIT, p);
+  if (rc) return rc;
+  if (n_steps < 0) return fail(H3_EINVAL, "n_steps < 0");
+  if (!sigmas) return fail(H3_EINVAL, "sigmas is NULL");
+  const DenoiseLayout dl = denoise_layout(p, n_blocks < 0 ? 0 : n_blocks);
+  if (!ws) return fail(H3_EINVAL, "workspace is NULL");
+  if (((uintptr_t)ws & 255) != 0) return fail(H3_EINVAL, "workspace must be 256-byte aligned");
+  if (ws_bytes < dl.total)
+    return fail(H3_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, dl.total);
+  if ((rc = check_dit_args(p, n_blocks, blocks, heads))) return rc;
+  if ((rc = check_time_weights(tw, n_blocks))) return rc;
+  if (!rows_w || rows_w->c_video != heads->c_video || rows_w->c_audio != heads->c_audio)
+    return fail(H3_EINVAL, "rows-in weights must match the head widths");
+  bf16_t* x = at<bf16_t>(ws, dl.x);
+  if ((rc = check_rows_in(shape, rows_w, text_rows, audio_latent, video_latent, x))) return rc;
+  if (rope && !aligned16(rope)) return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = upload_tables(p, ws, st))) return rc;
+  float* mod = at<float>(ws, dl.mod);
+  float* mod_final = at<float>(ws, dl.mod_final);
+  float* vv = at<float>(ws, dl.vel_video);
+  float* va = at<float>(ws, dl.vel_audio);
+  float* tscr = at<float>(ws, dl.time);
+  for (int k = 0; k < n_steps; ++k) {
+    const float* sg = sigmas + (size_t)3 * k;
+    const float* sn = sigmas + (size_t)3 * (k + 1);
+    if ((rc = run_rows_in(p.s, rows_w, text_rows, audio_latent, video_latent, x, st))) return rc;
+    if ((rc = run_modulation(p.H, n_blocks, tw, sg, mod, mod_final, tscr, st))) return rc;
+    if ((rc = run_dit(p, ws, n_blocks, blocks, heads, mod, mod_final, rope, x, vv, va, st)))
+      return rc;
+    prof_begin(H3_K_EULER, st);
+    H3_TRY(launch_euler(video_latent, vv, (size_t)p.s.n_video * heads->c_video,
+                        (double)sn[2] - (double)sg[2], st));
+    H3_TRY(launch_euler(audio_latent, va, (size_t)p.s.n_audio * heads->c_audio,
+                        (double)sn[1] - (double)sg[1], st));
+    prof_end(H3_K_EULER, st);
+  }
   return H3_OK;
 }
 
@@ -562,7 +769,8 @@ int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms) {
 
 const char* h3_prof_kernel_name(int32_t cls) {
   static const char* names[H3_K_COUNT] = {"modnorm", "gemm_qkv", "heads", "route", "attn",
-                                          "gemm_o", "gemm_fc1", "gemm_fc2", "final", "tables"};
+                                          "gemm_o", "gemm_fc1", "gemm_fc2", "final", "tables",
+                                          "rows_in", "time", "euler"};
   return (cls >= 0 && cls < H3_K_COUNT) ? names[cls] : "";
 }
 

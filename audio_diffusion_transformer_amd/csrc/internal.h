@@ -99,6 +99,29 @@ hipError_t launch_attn(int head_dim, const AttnArgs& a, hipStream_t s);
 hipError_t launch_out_head(const bf16_t* z, int rows, int H, const bf16_t* w, const bf16_t* b,
                            int C, float* vel, hipStream_t s);
 
+// ---- rows in, time conditioning, Euler -------------------------------------------
+struct RowsInArgs {
+  const bf16_t* text;                         // [n_text][H]
+  const float *audio, *video;                 // [n_audio][c_audio], [n_video][c_video]
+  const float *w_audio, *b_audio, *w_video, *b_video;  // [H][c], [H]
+  bf16_t* x;                                  // [R][H]
+  int n_text, n_audio, n_video, H, c_audio, c_video;
+};
+hipError_t launch_rows_in(const RowsInArgs& a, hipStream_t s);
+
+constexpr int kTimeEmbedDim = 256;  // width of the timestep frequency embedding
+
+struct TimeGemvArgs {
+  const float* in;        // [3][K] fp32, or null: the timestep embedding of sigma (K = 256)
+  const bf16_t *w, *b;    // [N][K], [N]
+  const bf16_t* table;    // null, or [n_blocks][N]: write out[l][s][o] = v + table[l][o]
+  float* out;             // [3][N], or [n_blocks][3][N] with a table
+  float sigma[3];
+  int K, N, n_blocks, in_silu, out_silu;
+};
+hipError_t launch_time_gemv(const TimeGemvArgs& a, hipStream_t s);
+hipError_t launch_euler(float* x, const float* v, size_t n, double dsigma, hipStream_t s);
+
 // ---- small table upload through kernel arguments ------------------------------
 hipError_t launch_poke(int* dst, const int* src, int n, hipStream_t s);
 

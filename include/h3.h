@@ -61,7 +61,7 @@ enum {
 
 enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2 };
 
-#define H3_ABI_VERSION 2
+#define H3_ABI_VERSION 3
 
 typedef struct {
   int32_t n_text, n_audio, n_video;  /* packed in this order */
@@ -102,6 +102,22 @@ typedef struct {
   const h3_bf16 *w_audio, *b_audio;  /* [c_audio][H], [c_audio] */
   int32_t c_video, c_audio;          /* each in [1, 256] */
 } h3_head_weights;
+
+/* F32 patch projections of the rows in (device). */
+typedef struct {
+  const float *w_video, *b_video;  /* [H][c_video], [H] */
+  const float *w_audio, *b_audio;  /* [H][c_audio], [H] */
+  int32_t c_video, c_audio;        /* patch widths, each in [1, 256] */
+} h3_rows_in_weights;
+
+/* Time embedder and modulation projections (bf16, device). */
+typedef struct {
+  const h3_bf16 *w1, *b1;            /* [H][256], [H] */
+  const h3_bf16 *w2, *b2;            /* [H][H], [H] */
+  const h3_bf16 *w_mod, *b_mod;      /* [6H][H], [6H] */
+  const h3_bf16 *mod_table;          /* [n_blocks][6][H]: per-block offsets */
+  const h3_bf16 *w_final, *b_final;  /* [2H][H], [2H] */
+} h3_time_weights;
 
 /* Byte offsets of the intermediates inside a block workspace (for tests and
  * diagnostics).  After h3_block_forward returns (and the stream is synced)
@@ -182,13 +198,57 @@ int h3_routed_attn(const h3_shape* shape, const int32_t* tile_start,
                    const h3_bf16* gate, h3_bf16* out, int32_t* sel, float* scores,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* The rows in (h3.c README, implementation notes: the F32 patch projections
+ * rounded straight into the packed hidden stream; TensorFold PR #949, "What
+ * it adds": the rows in):
+ *   x[text rows]  = text_rows (copied)
+ *   x[audio rows] = bf(audio_patch W_audio^T + b_audio)   F32 weights, inputs and sums
+ *   x[video rows] = bf(video_patch W_video^T + b_video)
+ * text_rows [n_text][H] bf16 (the text encoder's output); audio_patch
+ * [n_audio][c_audio], video_patch [n_video][c_video] fp32; x [R][H] bf16.
+ * All device pointers, 16-byte aligned.  No workspace. */
+int h3_rows_in(const h3_shape* shape, const h3_rows_in_weights* w, const h3_bf16* text_rows,
+               const float* audio_patch, const float* video_patch, h3_bf16* x, void* stream);
+
+/* The modulation tables of one denoising step from the per-segment timesteps
+ * sigma3 (HOST array: text, audio, video), TensorFold PR #949, "What comes
+ * next" (the time embedder and modulation tables).  With t = 1000 sigma_s:
+ *   e_s = [cos(t w_i)] ++ [sin(t w_i)], w_i = 10000^(-i/128), i < 128
+ *   c_s = W2 silu(W1 e_s + b1) + b2
+ *   mod[l][s]   = W_mod silu(c_s) + b_mod + mod_table[l]   fp32 [n_blocks][3][6][H]
+ *   mod_final[s] = W_final silu(c_s) + b_final             fp32 [3][2][H]
+ * ws: h3_modulation_workspace_bytes(shape) bytes of device scratch, 256-byte aligned. */
+size_t h3_modulation_workspace_bytes(const h3_shape* shape);
+int h3_modulation(const h3_shape* shape, int32_t n_blocks, const h3_time_weights* tw,
+                  const float* sigma3, float* mod, float* mod_final, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* The denoising loop on the device (h3.c README: Euler transitions, video and
+ * audio on independent schedules, a terminal zero after the last pass).  For
+ * each pass k < n_steps: the rows in from the current latents, the
+ * modulation tables of sigmas[k], the n_blocks-block forward and heads, then
+ *   video_latent += (sigmas[k+1][2] - sigmas[k][2]) vel_video
+ *   audio_latent += (sigmas[k+1][1] - sigmas[k][1]) vel_audio
+ * sigmas: HOST array [n_steps + 1][3] (text, audio, video); the latents
+ * (fp32 [n_video][c_video], [n_audio][c_audio], device) are updated in place.
+ * ws: h3_denoise_workspace_bytes(shape, tile_start, n_blocks) bytes. */
+size_t h3_denoise_workspace_bytes(const h3_shape* shape, const int32_t* tile_start,
+                                  int32_t n_blocks);
+int h3_denoise(const h3_shape* shape, int32_t n_blocks, int32_t n_steps,
+               const int32_t* tile_start, const h3_block_weights* blocks,
+               const h3_head_weights* heads, const h3_rows_in_weights* rows_w,
+               const h3_time_weights* tw, const float* sigmas, const float* rope,
+               const h3_bf16* text_rows, float* video_latent, float* audio_latent, void* ws,
+               size_t ws_bytes, void* stream);
+
 /* Kernel-time accounting for diagnostics: while enabled, each kernel launch
  * of the library is bracketed by HIP events on its stream.  h3_prof_read
  * synchronizes those events and returns, for kernel class `cls` (H3_K_*),
  * the launch count and the summed duration in milliseconds; it then forgets
  * the events it has read.  Not thread-safe; for benchmarks. */
 enum { H3_K_NORM = 0, H3_K_GEMM_QKV, H3_K_HEADS, H3_K_ROUTE, H3_K_ATTN, H3_K_GEMM_O,
-       H3_K_GEMM_FC1, H3_K_GEMM_FC2, H3_K_FINAL, H3_K_TABLES, H3_K_COUNT };
+       H3_K_GEMM_FC1, H3_K_GEMM_FC2, H3_K_FINAL, H3_K_TABLES, H3_K_ROWS_IN, H3_K_TIME,
+       H3_K_EULER, H3_K_COUNT };
 int h3_prof_enable(int on);
 int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms);
 const char* h3_prof_kernel_name(int32_t cls);

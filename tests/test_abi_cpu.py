@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.h3_abi_version() == 2
+    assert lib.h3_abi_version() == 3
 
 
 def _shape(sh):
@@ -126,3 +126,47 @@ def test_pages_block_shapes_are_accepted(lib):
         big_bytes = lay.q - lay.big
         assert big_bytes >= R * max(4 * A, F) * 2
         assert lay.x1 - lay.attn >= R * A * 2
+
+
+def test_denoise_entry_points_validate_before_launch(lib):
+    shape, ts = _shape(S.TINY)
+    tp = ts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    # rows in: missing weights, bad widths, unsupported hidden
+    rc = lib.h3_rows_in(ctypes.byref(shape), None, None, None, None, None, None)
+    assert rc == B.H3_EINVAL
+    rw = B.H3RowsInWeights(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                           ctypes.c_void_p(256), 300, 32)
+    rc = lib.h3_rows_in(ctypes.byref(shape), ctypes.byref(rw), ctypes.c_void_p(256),
+                        ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256), None)
+    assert rc == B.H3_EINVAL and "patch widths" in B.last_error()
+    bad = B.H3Shape.from_buffer_copy(shape)
+    bad.hidden = 300
+    rc = lib.h3_rows_in(ctypes.byref(bad), ctypes.byref(rw), None, None, None, None, None)
+    assert rc == B.H3_EUNSUPPORTED
+    # modulation: workspace size, missing sigma, missing weights, small workspace
+    n = lib.h3_modulation_workspace_bytes(ctypes.byref(shape))
+    assert n >= 6 * S.TINY.hidden * 4 and n % 256 == 0
+    assert lib.h3_modulation_workspace_bytes(ctypes.byref(bad)) == 0
+    tw = B.H3TimeWeights()
+    rc = lib.h3_modulation(ctypes.byref(shape), 2, ctypes.byref(tw), None, None, None, None, 0, None)
+    assert rc == B.H3_EINVAL and "sigma3" in B.last_error()
+    sig = (ctypes.c_float * 3)(1, 1, 1)
+    rc = lib.h3_modulation(ctypes.byref(shape), 2, ctypes.byref(tw), sig, None, None, None, 0, None)
+    assert rc == B.H3_EINVAL and "time weights" in B.last_error()
+    # denoise: its workspace extends the forward's; bad step counts and widths are refused
+    nd = lib.h3_denoise_workspace_bytes(ctypes.byref(shape), tp, 2)
+    assert nd > lib.h3_workspace_bytes(ctypes.byref(shape), tp, B.H3_WS_DIT)
+    assert lib.h3_denoise_workspace_bytes(ctypes.byref(shape), tp, 4) > nd
+    sig2 = (ctypes.c_float * 6)(1, 1, 1, 0, 0, 0)
+    rc = lib.h3_denoise(ctypes.byref(shape), 0, -1, tp, None, None, None, None, sig2, None, None,
+                        None, None, ctypes.c_void_p(256), 1 << 40, None)
+    assert rc == B.H3_EINVAL and "n_steps" in B.last_error()
+    hw = B.H3HeadWeights(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                         ctypes.c_void_p(256), 96, 32)
+    rw2 = B.H3RowsInWeights(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                            ctypes.c_void_p(256), 64, 32)
+    tw2 = B.H3TimeWeights(*[ctypes.c_void_p(256)] * 9)
+    rc = lib.h3_denoise(ctypes.byref(shape), 0, 1, tp, None, ctypes.byref(hw), ctypes.byref(rw2),
+                        ctypes.byref(tw2), sig2, None, None, None, None, ctypes.c_void_p(256),
+                        1 << 40, None)
+    assert rc == B.H3_EINVAL and "head widths" in B.last_error()
