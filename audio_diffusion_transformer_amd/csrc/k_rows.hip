@@ -7,9 +7,9 @@
 // accumulation and round each result straight into the packed hidden
 // stream); TensorFold PR #949, "What it adds" (the rows in).
 //   x[row][c] = bf( sum_k patch[row][k] W[c][k] + b[c] )   fp32, k ascending
-// One workgroup per 32 rows x 256 columns of one segment: 32-wide k slices
-// of W (transposed) and of the patches are staged in LDS; each thread owns
-// 4 rows x 8 consecutive columns and writes them as 16-byte bf16 runs.  Text
+// One workgroup per 64 rows x 256 columns of one segment: 32-wide k slices
+// of W and of the patches are staged in LDS (both k-major); each thread owns
+// 8 rows x 8 consecutive columns and writes them as 16-byte bf16 runs.  Text
 // rows (the text encoder's output) are copied as they are.
 //
 // Time conditioning: TensorFold PR #949, "What comes next" (the time embedder
@@ -19,9 +19,9 @@
 //   h_s  = silu(W1 e_s + b1);  c_s = W2 h_s + b2
 //   mod[l][s] = W_mod silu(c_s) + b_mod + table[l];  final[s] = W_final silu(c_s) + b_final
 // as four matrix-vector products over the three segments at once: a
-// workgroup stages the three input vectors (fp32) in LDS, each wave takes 4
-// output rows and reads its weight rows once with 16-byte loads (the
-// products are bound by reading the bf16 weights from HBM).
+// workgroup (8 waves) stages the three input vectors (fp32) in LDS, each wave
+// takes 8 output rows, two at a time, and reads its weight rows once with
+// 16-byte loads (the products are bound by reading the bf16 weights from HBM).
 //
 // Euler: h3.c README (Euler transitions; video and audio on independent
 // schedules, a terminal zero after the last pass):
@@ -35,7 +35,7 @@ namespace {
 
 // ---- rows in ---------------------------------------------------------------
 
-constexpr int kRiRows = 32, kRiCols = 256, kRiK = 32;
+constexpr int kRiRows = 64, kRiCols = 256, kRiK = 32;
 
 __global__ __launch_bounds__(256) void k_rows_in(RowsInArgs a) {
   const int seg = blockIdx.z;  // 0 text, 1 audio, 2 video
@@ -61,11 +61,11 @@ __global__ __launch_bounds__(256) void k_rows_in(RowsInArgs a) {
   const int C = seg == 1 ? a.c_audio : a.c_video;
 
   __shared__ __attribute__((aligned(16))) float sW[kRiK][kRiCols + 4];  // [k][column]
-  __shared__ float sP[kRiRows][kRiK + 1];                               // [row][k]
-  const int cg = tid & 31, rg = tid >> 5;  // columns 8 cg .. 8 cg + 7; rows rg + 8 i
-  float acc[4][8];
+  __shared__ __attribute__((aligned(16))) float sP[kRiK][kRiRows + 4];  // [k][row]
+  const int cg = tid & 31, rg = tid >> 5;  // columns 8 cg .. 8 cg + 7; rows 8 rg .. 8 rg + 7
+  float acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
   for (int k0 = 0; k0 < C; k0 += kRiK) {
@@ -76,29 +76,28 @@ __global__ __launch_bounds__(256) void k_rows_in(RowsInArgs a) {
     }
     for (int idx = tid; idx < kRiRows * kRiK; idx += 256) {
       const int r = idx / kRiK, k = idx % kRiK;
-      sP[r][k] = (m0 + r < nrows && k0 + k < C) ? patch[(size_t)(m0 + r) * C + k0 + k] : 0.f;
+      sP[k][r] = (m0 + r < nrows && k0 + k < C) ? patch[(size_t)(m0 + r) * C + k0 + k] : 0.f;
     }
     __syncthreads();
-#pragma unroll 4
+#pragma unroll 2
     for (int k = 0; k < kRiK; ++k) {
       const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(&sW[k][8 * cg]);
       const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(&sW[k][8 * cg + 4]);
+      const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(&sP[k][8 * rg]);
+      const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(&sP[k][8 * rg + 4]);
+      const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = sP[rg + 8 * i][k];
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = fmaf(p, w0[j], acc[i][j]);
-          acc[i][4 + j] = fmaf(p, w1[j], acc[i][4 + j]);
-        }
-      }
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(pv[i], wv[j], acc[i][j]);
     }
   }
   const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(bias + n0 + 8 * cg);
   const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(bias + n0 + 8 * cg + 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = rg + 8 * i;
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * rg + i;
     if (m0 + r >= nrows) continue;
     u32x4_t w;
 #pragma unroll
@@ -112,18 +111,44 @@ __global__ __launch_bounds__(256) void k_rows_in(RowsInArgs a) {
 
 // ---- time conditioning: out[s][o] = W[o] . act(in[s]) + b[o], s < 3 --------
 
-constexpr int kTvRowsPerWave = 4;
+constexpr int kTvWaves = 8, kTvRowsPerWave = 8;
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
-__global__ __launch_bounds__(256) void k_time_gemv(TimeGemvArgs a) {
+// dot products of weight row `wr` (bf16, K) with the three staged inputs; the
+// lane takes the 16-byte units lane, lane + 64, ...
+__device__ __forceinline__ void dot3(const bf16_t* __restrict__ wr, const float* sIn, int K,
+                                     int lane, float& a0, float& a1, float& a2) {
+  for (int k8 = lane * 8; k8 < K; k8 += 512) {
+    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(wr + k8);
+    float wf[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      wf[2 * t] = bflo(wv[t]);
+      wf[2 * t + 1] = bfhi(wv[t]);
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      const f32x4_t i0 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8]);
+      const f32x4_t i1 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8 + 4]);
+      float acc = s == 0 ? a0 : (s == 1 ? a1 : a2);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = fmaf(wf[t], i0[t], acc);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = fmaf(wf[4 + t], i1[t], acc);
+      if (s == 0) a0 = acc; else if (s == 1) a1 = acc; else a2 = acc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * kTvWaves) void k_time_gemv(TimeGemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sIn[];  // [3][K]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K;
   if (a.in == nullptr) {
     // the frequency embedding of t_s = 1000 sigma_s (fp64 arguments, so the
     // large angles keep their accuracy)
-    for (int idx = tid; idx < 3 * K; idx += 256) {
+    for (int idx = tid; idx < 3 * K; idx += 64 * kTvWaves) {
       const int s = idx / K, i = idx % K, half = K / 2;
       const int f = i < half ? i : i - half;
       const double om = exp(-9.210340371976184 * (double)f / (double)half);  // 10000^(-f/half)
@@ -131,52 +156,39 @@ __global__ __launch_bounds__(256) void k_time_gemv(TimeGemvArgs a) {
       sIn[idx] = (float)(i < half ? cos(ang) : sin(ang));
     }
   } else {
-    for (int idx = tid; idx < 3 * K; idx += 256) {
-      const float v = a.in[idx];
-      sIn[idx] = a.in_silu ? silu_f(v) : v;
+    for (int idx = 4 * tid; idx < 3 * K; idx += 4 * 64 * kTvWaves) {
+      f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.in + idx);
+      if (a.in_silu)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = silu_f(v[t]);
+      *reinterpret_cast<f32x4_t*>(&sIn[idx]) = v;
     }
   }
   __syncthreads();
-  const int o0 = (blockIdx.x * 4 + wave) * kTvRowsPerWave;
-#pragma unroll
-  for (int rr = 0; rr < kTvRowsPerWave; ++rr) {
+  const int o0 = (blockIdx.x * kTvWaves + wave) * kTvRowsPerWave;
+  for (int rr = 0; rr < kTvRowsPerWave; rr += 2) {
     const int o = o0 + rr;
     if (o >= a.N) break;  // uniform over the wave
-    const bf16_t* wr = a.w + (size_t)o * K;
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f;
-    for (int k8 = lane * 8; k8 < K; k8 += 512) {
-      const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(wr + k8);
-      float wf[8];
+    const bool two = o + 1 < a.N;
+    float x0 = 0.f, x1 = 0.f, x2 = 0.f, y0 = 0.f, y1 = 0.f, y2 = 0.f;
+    dot3(a.w + (size_t)o * K, sIn, K, lane, x0, x1, x2);
+    if (two) dot3(a.w + (size_t)(o + 1) * K, sIn, K, lane, y0, y1, y2);
+    x0 = wave_sum(x0); x1 = wave_sum(x1); x2 = wave_sum(x2);
+    y0 = wave_sum(y0); y1 = wave_sum(y1); y2 = wave_sum(y2);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        wf[2 * t] = bflo(wv[t]);
-        wf[2 * t + 1] = bfhi(wv[t]);
-      }
-      float* accs[3] = {&acc0, &acc1, &acc2};
-#pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        const f32x4_t i0 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8]);
-        const f32x4_t i1 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8 + 4]);
-        float acc = *accs[s];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc = fmaf(wf[t], i0[t], acc);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc = fmaf(wf[4 + t], i1[t], acc);
-        *accs[s] = acc;
-      }
-    }
-    acc0 = wave_sum(acc0);
-    acc1 = wave_sum(acc1);
-    acc2 = wave_sum(acc2);
-    if (lane < 3) {
-      const float b = bf2f(a.b[o]);
-      float v = (lane == 0 ? acc0 : (lane == 1 ? acc1 : acc2)) + b;
-      if (a.out_silu) v = silu_f(v);
-      if (a.table == nullptr) {
-        a.out[(size_t)lane * a.N + o] = v;
-      } else {  // modulation tables: mod[l][s][o] = v + table[l][o]
-        for (int l = 0; l < a.n_blocks; ++l)
-          a.out[((size_t)l * 3 + lane) * a.N + o] = v + bf2f(a.table[(size_t)l * a.N + o]);
+    for (int q = 0; q < 2; ++q) {
+      const int oo = o + q;
+      if (lane < 3 && (q == 0 || two)) {
+        const float sum = q == 0 ? (lane == 0 ? x0 : (lane == 1 ? x1 : x2))
+                                 : (lane == 0 ? y0 : (lane == 1 ? y1 : y2));
+        float v = sum + bf2f(a.b[oo]);
+        if (a.out_silu) v = silu_f(v);
+        if (a.table == nullptr) {
+          a.out[(size_t)lane * a.N + oo] = v;
+        } else {  // modulation tables: mod[l][s][o] = v + table[l][o]
+          for (int l = 0; l < a.n_blocks; ++l)
+            a.out[((size_t)l * 3 + lane) * a.N + oo] = v + bf2f(a.table[(size_t)l * a.N + oo]);
+        }
       }
     }
   }
@@ -202,9 +214,10 @@ hipError_t launch_rows_in(const RowsInArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_time_gemv(const TimeGemvArgs& a, hipStream_t s) {
-  const int rows_per_wg = 4 * kTvRowsPerWave;
+  const int rows_per_wg = kTvWaves * kTvRowsPerWave;
   dim3 grid((a.N + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL(k_time_gemv, grid, dim3(256), (size_t)3 * a.K * sizeof(float), s, a);
+  hipLaunchKernelGGL(k_time_gemv, grid, dim3(64 * kTvWaves), (size_t)3 * a.K * sizeof(float), s,
+                     a);
   return hipGetLastError();
 }
 

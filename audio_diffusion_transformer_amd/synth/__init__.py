@@ -385,3 +385,13 @@ def device_block_weights(shape: Shape, block: int = 0, seed: int = SEED, std: fl
         mean = 1.0 if k in ("q_gain", "k_gain") else 0.0
         w[k] = device_normal_bf16(p + k, shp, std, seed, device, mean=mean)
     return w
+
+
+def device_time_weights(shape: Shape, n_blocks: int, seed: int = SEED, std: float = 0.02,
+                        device="cuda"):
+    """time_weights drawn on the device (same shapes and distribution)."""
+    H = shape.hidden
+    shapes = {"w1": (H, T_EMBED_DIM), "b1": (H,), "w2": (H, H), "b2": (H,),
+              "w_mod": (6 * H, H), "b_mod": (6 * H,), "mod_table": (n_blocks, 6, H),
+              "w_final": (2 * H, H), "b_final": (2 * H,)}
+    return {k: device_normal_bf16("time." + k, shp, std, seed, device) for k, shp in shapes.items()}

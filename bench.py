@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 N_BLOCKS = 50
+N_PASSES = 8                # denoising passes of --denoise (the pages' 8-step schedule)
 PAGES_FASTH3_S = 10.1       # the pages' 50-block FastH3 forward, median of steps 2-8, M5 Ultra
 
 
@@ -49,6 +50,9 @@ def parse():
                     help="full: the default 50-block forward (hidden 5120, GELU); fasth3: the "
                          "pages' own block and geometry (hidden 5376, 56x128 heads, SwiGLU "
                          "14336, routing gate, cube tiles, top-k 56)")
+    ap.add_argument("--denoise", action="store_true",
+                    help="time h3_denoise instead: 8 passes of rows in, modulation tables, "
+                         "the 50-block forward and heads, and the Euler step, per timed step")
     ap.add_argument("--attn-sweep", action="store_true",
                     help="only time h3_routed_attn at 15,435 rows x 40 heads x 128 over tile "
                          "size {32, 64, 128} x top-k {8, 32, all}; one JSON line per case")
@@ -92,6 +96,89 @@ def measured_traffic(kernel):
         return None
     return round(TRAFFIC["fetch_kib"] * 1024 * TRAFFIC["fetch_scale"] +
                  TRAFFIC["write_kib"] * 1024 * TRAFFIC["write_scale"])
+
+
+def denoise_bench(args):
+    """The denoising loop on the device: each timed step is one h3_denoise call
+    of N_PASSES passes (rows in from the fp32 latents, modulation tables from the
+    timesteps, the 50-block forward and heads, Euler step of the latents) on the
+    default workload, the same initial latents every step."""
+    import torch
+    from audio_diffusion_transformer_amd import binding as B
+    from audio_diffusion_transformer_amd import synth as S
+    from audio_diffusion_transformer_amd import tensors as T
+    global WORKLOAD
+    WORKLOAD = args.workload
+    sh = S.FASTH3 if args.workload == "fasth3" else S.FULL
+    L = args.blocks
+    n_pass = N_PASSES
+    ts, npt = S.tile_map(sh)
+    shape = B.make_shape(sh, ts, npt)
+    torch.cuda.set_device(0)
+    print(f"setup: {L} blocks of weights, time weights", file=sys.stderr, flush=True)
+    blocks = [S.device_block_weights(sh, block=l) for l in range(L)]
+    warr = (B.H3BlockWeights * L)(*[B.block_weights_struct(b) for b in blocks])
+    heads = B.head_weights_struct(hd := {k: T.to_dev(v) for k, v in S.head_weights(sh).items()})
+    rw = {k: torch.from_numpy(v).cuda() for k, v in S.rows_in_weights(sh).items()}
+    tw = S.device_time_weights(sh, L)
+    rope = T.to_dev(S.rope_tables(sh))
+    text = T.to_dev(S.text_rows(sh))
+    lv0, la0 = (torch.from_numpy(a).cuda() for a in S.latents(sh))
+    lv, la = lv0.clone(), la0.clone()
+    sig = S.schedule(n_pass)
+    ws = T.workspace(B.denoise_workspace_bytes(shape, ts, L))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def run():
+        lv.copy_(lv0)
+        la.copy_(la0)
+        B.denoise(shape, ts, warr, heads, rw, tw, sig, rope, text, lv, la, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    print(f"warmup done ({args.warmup})", file=sys.stderr, flush=True)
+    if not args.no_prof:
+        B.prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = B.prof_read() if not args.no_prof else {}
+    B.prof_enable(False)
+    ms = (t1 - t0) * 1e3 / args.steps
+    fin = np.isfinite(lv.cpu().numpy()).all() and np.isfinite(la.cpu().numpy()).all()
+    H, R = sh.hidden, sh.rows
+    work = {  # algorithmic bytes per launch of the three small kernels
+        "rows_in": ("hbm", 4.0 * (sh.n_video * sh.c_video + sh.n_audio * sh.c_audio)
+                    + 2.0 * sh.n_text * H + 2.0 * R * H),
+        "time": ("hbm", 2.0 * (256 * H + H * H + (6 * H * H if L else 0) + 2 * H * H)
+                 + 4.0 * 3 * (6 * H * L + 2 * H)),
+    }
+    kernels = {}
+    for name, (n, tms) in kern.items():
+        if n == 0:
+            continue
+        e = {"launches": n, "avg_ms": round(tms / n, 4), "total_ms": round(tms, 2)}
+        if name in work:
+            gbs = work[name][1] / (tms / n * 1e-3) / 1e9
+            e.update(achieved_gbs=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[name] = e
+    line = {
+        "metric": f"s per {n_pass}-pass denoise (rows in, modulation tables, {L}-block "
+                  f"forward and heads, Euler step per pass) at {R:,} rows",
+        "value": round(ms / 1e3, 4), "unit": "s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 2), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload} geometry, {L} blocks, {n_pass} passes, "
+                               f"shifted linear schedule with the terminal zero, seeded "
+                               f"random weights and latents", "rows": R, "hidden": H},
+        "latents_finite": bool(fin), "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def attn_sweep():
@@ -246,6 +333,9 @@ def main():
         return
     if args.attn_sweep:
         attn_sweep()
+        return
+    if args.denoise:
+        denoise_bench(args)
         return
 
     import torch
