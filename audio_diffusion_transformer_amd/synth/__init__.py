@@ -211,13 +211,39 @@ def tile_map(shape: Shape):
     return np.asarray(starts, dtype=np.int32), n_prefix_tiles
 
 
-def rope_tables(shape: Shape):
+def token_pairs(shape: Shape):
+    """The reduced video sequence of token reduction: horizontally adjacent
+    tokens (t, h, 2j) and (t, h, 2j + 1) of the video grid become one token;
+    with an odd width the last column stays single.  The reduced grid
+    (T, H, ceil(W/2)) is stored cube by cube like the full one.
+
+    Returns (reduced shape, pairs int32 [V'][2] of full video row indices
+    (second -1 for a single token), positions: the full-grid raster index of
+    each reduced token's first token, for its rotary angle)."""
+    T, Hh, W = shape.video_grid
+    Wr = (W + 1) // 2
+    red = shape.replace(n_video=T * Hh * Wr, video_grid=(T, Hh, Wr))
+    full_pos = video_positions(shape)
+    row_of = np.empty(shape.n_video, dtype=np.int64)
+    row_of[full_pos] = np.arange(shape.n_video)
+    rpos = video_positions(red)  # reduced raster index of every reduced row, in storage order
+    t, rem = np.divmod(rpos, Hh * Wr)
+    h, w = np.divmod(rem, Wr)
+    first = t * Hh * W + h * W + 2 * w
+    has2 = 2 * w + 1 < W
+    pairs = np.stack([row_of[first], np.where(has2, row_of[np.minimum(first + 1, T * Hh * W - 1)], -1)],
+                     axis=1).astype(np.int32)
+    return red, pairs, first
+
+
+def rope_tables(shape: Shape, video_pos=None):
     """fp32 [R][d/2][2] (cos, sin); position = row index within its segment
-    (for video rows stored by cubes: the raster index), angle_i = pos *
-    10000^(-2i/d)."""
+    (for video rows stored by cubes: the raster index; or the given
+    video_pos), angle_i = pos * 10000^(-2i/d)."""
     d2 = shape.head_dim // 2
+    vpos = video_positions(shape) if video_pos is None else np.asarray(video_pos)
     pos = np.concatenate([np.arange(shape.n_text), np.arange(shape.n_audio),
-                          video_positions(shape)]).astype(np.float64)
+                          vpos]).astype(np.float64)
     inv = 10000.0 ** (-2.0 * np.arange(d2, dtype=np.float64) / shape.head_dim)
     ang = pos[:, None] * inv[None, :]
     out = np.empty((shape.rows, d2, 2), dtype=np.float32)

@@ -42,7 +42,11 @@ bf16; the time embedder is a 256-wide cos/sin frequency embedding of
 t = 1000 sigma followed by Linear -> silu -> Linear; the modulation tables of
 a step are one shared projection of silu(c) per segment plus a per-block
 table, stored fp32; each pass ends with an Euler transition of the fp32
-latents on the caller's per-segment schedule.
+latents on the caller's per-segment schedule.  Token reduction: a pair of
+horizontally adjacent video tokens pools to the bf16 mean of the two; the
+restore adds the pair's update (current minus pooled value) to each token's
+value at the pooling point and rounds once; a single token (odd width) takes
+its reduced value; the pooled token rotates by its first token's position.
 
 Parity against a released H3 / FastH3 checkpoint is unpinned (no weights,
 case file or reference velocities are available); every function here is
@@ -543,3 +547,76 @@ def denoise(sh, tile_start, n_prefix_tiles, blocks, head, rows_w, tw, sigmas, ro
         lat_v = euler_step(lat_v, r["vel_video"], sig[k][2], sig[k + 1][2])
         lat_a = euler_step(lat_a, r["vel_audio"], sig[k][1], sig[k + 1][1])
     return dict(video=lat_v, audio=lat_a, vels=vels)
+
+
+# ----------------------------------------------------------------------------
+# Token reduction
+# ----------------------------------------------------------------------------
+
+def token_pool(x, pairs, n_prefix):
+    """The reduced stream (h3.c README, implementation notes: token reduction
+    pairs adjacent horizontal video tokens and leaves text and audio rows as
+    they are): prefix rows unchanged; reduced video row r = bf((x[a] + x[b]) / 2)
+    for its pair (a, b) of full video rows, x[a] for a single token.
+    x: float64 bf16 values [P + V][H]; pairs int [V'][2] (-1: single).
+    Returns [P + V'][H]."""
+    P = n_prefix
+    v = x[P:]
+    a, b = pairs[:, 0], pairs[:, 1]
+    single = b < 0
+    pooled = round_bf16((v[a] + v[np.where(single, a, b)]) / 2.0)
+    pooled[single] = v[a[single]]
+    return np.concatenate([x[:P], pooled], axis=0)
+
+
+def token_restore(x_red, orig, baseline, pairs, n_prefix, n_video):
+    """Back to full resolution (h3.c README: each token returns as its
+    original value plus the update learned by its pair): video row i of pair r
+    = bf(orig[i] + (x_red[r] - baseline[r])), baseline the pair's pooled
+    value when it was formed; a single token takes x_red[r]; prefix rows take
+    their reduced-stream values.  orig: the full stream when it was reduced."""
+    P = n_prefix
+    out = np.empty((P + n_video, x_red.shape[1]))
+    out[:P] = x_red[:P]
+    a, b = pairs[:, 0], pairs[:, 1]
+    single = b < 0
+    upd = x_red[P:] - baseline[P:]
+    out[P + a[single]] = x_red[P:][single]
+    out[P + a[~single]] = round_bf16(orig[P + a[~single]] + upd[~single])
+    out[P + b[~single]] = round_bf16(orig[P + b[~single]] + upd[~single])
+    return out
+
+
+def dit_forward_reduced(sh, tile_start, n_prefix_tiles, red_sh, red_tile_start, red_npt, pairs,
+                        reduce_at, restore_at, blocks, head, mods, mod_final, rope, red_rope, x_in):
+    """The forward with token reduction (h3.c README, implementation notes):
+    blocks [0, reduce_at) at full resolution, then the pooled stream through
+    blocks [reduce_at, restore_at) (its own tile map and rotary table), the
+    restore against the full-resolution state kept at the pooling point, and
+    blocks [restore_at, L) at full resolution; then the final norm and heads."""
+    x_bits = np.asarray(x_in, dtype=np.uint16)
+    x = bf16_to_f64(x_bits)
+    P = sh.n_text + sh.n_audio
+    L = len(blocks)
+    assert 0 <= reduce_at <= restore_at <= L
+    orig = base = None
+    for l in range(L):
+        if l == reduce_at and reduce_at < restore_at:
+            orig = x
+            x = token_pool(x, pairs, P)
+            base = x
+            x_bits = f64_to_bf16_bits(x)
+        if l == restore_at and orig is not None:
+            x = token_restore(x, orig, base, pairs, P, sh.n_video)
+            x_bits = f64_to_bf16_bits(x)
+            orig = None
+        if orig is None:
+            r = block_forward(sh, tile_start, n_prefix_tiles, blocks[l], mods[l], rope, x_bits)
+        else:
+            r = block_forward(red_sh, red_tile_start, red_npt, blocks[l], mods[l], red_rope, x_bits)
+        x = r["x2"]
+        x_bits = f64_to_bf16_bits(x)
+    if orig is not None:  # restore_at == L
+        x = token_restore(x, orig, base, pairs, P, sh.n_video)
+    vv, va = final_heads(sh, x, mod_final, head)
+    return dict(x=x, vel_video=vv, vel_audio=va)

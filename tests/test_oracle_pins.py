@@ -688,3 +688,75 @@ def test_denoise_with_constant_heads_follows_the_schedules():
     np.testing.assert_allclose(r["video"], lv - 0.5, atol=1e-6)
     np.testing.assert_allclose(r["audio"], la + 0.25 * 0.75, atol=1e-6)
     assert len(r["vels"]) == 3
+
+
+# ----------------------------------------------------------------------------
+# Token reduction
+# ----------------------------------------------------------------------------
+
+def test_token_pairs_cover_the_grid_with_horizontal_neighbours():
+    from audio_diffusion_transformer_amd import synth as S
+    for sh in (S.FASTH3_TINY, S.FASTH3):
+        red, pairs, first = S.token_pairs(sh)
+        T, Hh, W = sh.video_grid
+        assert red.n_video == T * Hh * ((W + 1) // 2)
+        used = np.concatenate([pairs[:, 0], pairs[pairs[:, 1] >= 0, 1]])
+        np.testing.assert_array_equal(np.sort(used), np.arange(sh.n_video))
+        pos = S.video_positions(sh)          # raster index of every full video row
+        a, b = pairs[:, 0], pairs[:, 1]
+        two = b >= 0
+        np.testing.assert_array_equal(pos[a], first)
+        np.testing.assert_array_equal(pos[b[two]], pos[a[two]] + 1)   # right-hand neighbour
+        np.testing.assert_array_equal(pos[a] % W % 2, 0)              # pairs start on even columns
+        assert np.all(pos[a[~two]] % W == W - 1)                      # singles: the odd last column
+        assert (~two).sum() == (T * Hh if W % 2 else 0)
+
+
+def test_token_pool_and_restore_hand_example():
+    P = 1
+    x = np.array([[9.0, 9.0], [1.0, 2.0], [3.0, 5.0], [7.0, -1.0]])   # prefix, then 3 video rows
+    pairs = np.array([[1, 0], [2, -1]])                               # (v1, v0) and v2 single
+    r = O.token_pool(x, pairs, P)
+    np.testing.assert_array_equal(r, [[9.0, 9.0], [2.0, 3.5], [7.0, -1.0]])
+    # no update: exactly the original stream
+    np.testing.assert_array_equal(O.token_restore(r, x, r, pairs, P, 3), x)
+    # an update d of a pair returns to both its tokens; a single takes its value
+    upd = r.copy()
+    upd[0] += 0.5
+    upd[1] += [0.25, -2.0]
+    upd[2] = [4.0, 4.0]
+    out = O.token_restore(upd, x, r, pairs, P, 3)
+    np.testing.assert_array_equal(out, [[9.5, 9.5], [1.25, 0.0], [3.25, 3.0], [4.0, 4.0]])
+
+
+def test_token_pool_rounds_the_mean_once():
+    # (1 + (1 + 2^-7)) / 2 = 1 + 2^-8: a tie between bf16 1.0 and 1 + 2^-7 -> even (1.0)
+    x = np.array([[1.0], [1.0 + 2 ** -7]])
+    r = O.token_pool(x, np.array([[0, 1]]), 0)
+    assert r[0, 0] == 1.0
+
+
+def test_reduced_forward_with_identity_middle_equals_the_outer_blocks():
+    """Zero gates make the reduced blocks the identity, so the restore must
+    give back the pooled-from state bit for bit and the forward equals the
+    full forward over the outer blocks alone."""
+    from audio_diffusion_transformer_amd import synth as S
+    sh = S.FASTH3_TINY
+    ts, npt = S.tile_map(sh)
+    red, pairs, first = S.token_pairs(sh)
+    rts, rnpt = S.tile_map(red)
+    L, r0, r1 = 4, 1, 3
+    blocks = [S.block_weights(sh, block=l) for l in range(L)]
+    mods = np.stack([S.modulation(sh, block=l) for l in range(L)])
+    mods[r0:r1, :, 2, :] = 0
+    mods[r0:r1, :, 5, :] = 0
+    head = S.head_weights(sh)
+    mf = S.final_modulation(sh)
+    x = S.activations(sh, field=True)
+    got = O.dit_forward_reduced(sh, ts, npt, red, rts, rnpt, pairs, r0, r1, blocks, head, mods, mf,
+                                S.rope_tables(sh), S.rope_tables(red, first), x)
+    keep = [l for l in range(L) if not r0 <= l < r1]
+    ref = O.dit_forward(sh, ts, npt, [blocks[l] for l in keep], head, mods[keep], mf,
+                        S.rope_tables(sh), x)
+    np.testing.assert_array_equal(got["vel_video"], ref["vel_video"])
+    np.testing.assert_array_equal(got["vel_audio"], ref["vel_audio"])
