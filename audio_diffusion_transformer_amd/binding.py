@@ -20,7 +20,7 @@ H3_WS_BLOCK, H3_WS_DIT, H3_WS_ATTN = 0, 1, 2
 ABI_VERSION = 3  # must match H3_ABI_VERSION in include/h3.h
 
 KERNEL_CLASSES = ["modnorm", "gemm_qkv", "heads", "route", "attn", "gemm_o", "gemm_fc1",
-                  "gemm_fc2", "final", "tables", "rows_in", "time", "euler"]
+                  "gemm_fc2", "final", "tables", "rows_in", "time", "euler", "tokens"]
 
 _vp = ctypes.c_void_p
 
@@ -53,6 +53,12 @@ class H3RowsInWeights(ctypes.Structure):
 class H3TimeWeights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("w1", "b1", "w2", "b2", "w_mod", "b_mod", "mod_table",
                                    "w_final", "b_final")]
+
+
+class H3TokenReduction(ctypes.Structure):
+    _fields_ = [("reduced", ctypes.POINTER(H3Shape)), ("tile_start", ctypes.POINTER(ctypes.c_int32)),
+                ("pairs", _vp), ("rope", _vp), ("reduce_at", ctypes.c_int32),
+                ("restore_at", ctypes.c_int32)]
 
 
 class H3WsLayout(ctypes.Structure):
@@ -108,13 +114,21 @@ def lib():
                              ctypes.POINTER(H3BlockWeights), ctypes.POINTER(H3HeadWeights),
                              ctypes.POINTER(H3RowsInWeights), ctypes.POINTER(H3TimeWeights),
                              f32p, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.h3_dit_forward_tr_workspace_bytes.argtypes = [ctypes.POINTER(H3Shape), i32p,
+                                                    ctypes.POINTER(H3TokenReduction)]
+    L.h3_dit_forward_tr_workspace_bytes.restype = ctypes.c_size_t
+    L.h3_dit_forward_tr.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32, i32p,
+                                    ctypes.POINTER(H3TokenReduction),
+                                    ctypes.POINTER(H3BlockWeights), ctypes.POINTER(H3HeadWeights),
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.h3_prof_enable.argtypes = [ctypes.c_int]
     L.h3_prof_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                ctypes.POINTER(ctypes.c_double)]
     L.h3_prof_kernel_name.argtypes = [ctypes.c_int32]
     L.h3_prof_kernel_name.restype = ctypes.c_char_p
     for f in (L.h3_workspace_layout, L.h3_block_forward, L.h3_dit_forward, L.h3_routed_attn,
-              L.h3_rows_in, L.h3_modulation, L.h3_denoise, L.h3_prof_enable, L.h3_prof_read):
+              L.h3_rows_in, L.h3_modulation, L.h3_denoise, L.h3_dit_forward_tr,
+              L.h3_prof_enable, L.h3_prof_read):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -273,6 +287,40 @@ def denoise(shape, tile_start, blocks, heads, rows_w, tw, sigmas, rope, text_row
                             ctypes.byref(rw), ctypes.byref(tws), sp, _ptr(rope), _ptr(text_rows),
                             _ptr(video_latent), _ptr(audio_latent), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class TokenReduction:
+    """Keeps the C struct and the host arrays it points to alive together."""
+
+    def __init__(self, red_shape: H3Shape, red_tile_start, pairs, rope, reduce_at, restore_at):
+        self.shape = red_shape
+        self.ts, tp = _tiles(red_tile_start)
+        self.pairs, self.rope = pairs, rope
+        self.c = H3TokenReduction(ctypes.pointer(self.shape), tp, _ptr(pairs), _ptr(rope),
+                                  int(reduce_at), int(restore_at))
+
+
+def dit_forward_tr_workspace_bytes(shape, tile_start, tr: TokenReduction):
+    ts, tp = _tiles(tile_start)
+    n = lib().h3_dit_forward_tr_workspace_bytes(ctypes.byref(shape), tp, ctypes.byref(tr.c))
+    if n == 0:
+        raise H3Error(H3_EINVAL, last_error())
+    return n
+
+
+def dit_forward_tr(shape, tile_start, tr: TokenReduction, blocks, heads, mod, mod_final, rope,
+                   x_in, vel_video, vel_audio, ws, stream=None):
+    ts, tp = _tiles(tile_start)
+    if isinstance(blocks, (list, tuple)):
+        arr = (H3BlockWeights * max(len(blocks), 1))(*[block_weights_struct(b) for b in blocks])
+        n = len(blocks)
+    else:
+        arr, n = blocks, len(blocks)
+    hw = head_weights_struct(heads) if isinstance(heads, dict) else heads
+    _check(lib().h3_dit_forward_tr(ctypes.byref(shape), n, tp, ctypes.byref(tr.c), arr,
+                                   ctypes.byref(hw), _ptr(mod), _ptr(mod_final), _ptr(rope),
+                                   _ptr(x_in), _ptr(vel_video), _ptr(vel_audio), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def prof_enable(on=True):

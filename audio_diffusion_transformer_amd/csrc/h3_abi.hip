@@ -518,6 +518,46 @@ DenoiseLayout denoise_layout(const Plan& p, int n_blocks) {
   return d;
 }
 
+struct TrLayout {
+  size_t orig, red, full, total;
+};
+
+// the larger of the two forward workspaces, then the kept video rows, the
+// pooled stream as formed (the restore's baseline) and the restored stream
+TrLayout tr_layout(const Plan& pf, const Plan& pr) {
+  TrLayout t{};
+  size_t off = align256(pf.lay.total > pr.lay.total ? pf.lay.total : pr.lay.total);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  t.orig = take((size_t)(pf.s.n_video > 0 ? pf.s.n_video : 1) * pf.H * 2);
+  t.red = take((size_t)pr.R * pr.H * 2);
+  t.full = take((size_t)pf.R * pf.H * 2);
+  t.total = off;
+  return t;
+}
+
+int tr_plans(const h3_shape* shape, const int32_t* tile_start, const h3_token_reduction* tr,
+             Plan& pf, Plan& pr) {
+  int rc = make_plan(shape, tile_start, H3_WS_DIT, pf);
+  if (rc) return rc;
+  if (!tr || !tr->reduced || !tr->tile_start) return fail(H3_EINVAL, "token reduction is NULL");
+  h3_shape rs = *tr->reduced;
+  if (rs.n_text != shape->n_text || rs.n_audio != shape->n_audio || rs.hidden != shape->hidden ||
+      rs.n_heads != shape->n_heads || rs.head_dim != shape->head_dim || rs.ffn != shape->ffn ||
+      rs.top_k != shape->top_k || rs.pooled != shape->pooled || rs.norm_eps != shape->norm_eps ||
+      rs.mlp != shape->mlp || rs.gate != shape->gate)
+    return fail(H3_EINVAL, "the reduced shape may differ from the full one only in its video rows "
+                           "and tile map");
+  if (rs.n_video < 0 || rs.n_video > shape->n_video)
+    return fail(H3_EINVAL, "the reduced stream has %d video rows, the full one %d", rs.n_video,
+                shape->n_video);
+  if ((rc = make_plan(&rs, tr->tile_start, H3_WS_DIT, pr))) return rc;
+  return H3_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Kernel-time accounting
 // ---------------------------------------------------------------------------
@@ -716,6 +756,93 @@ int h3_denoise(const h3_shape* shape, int32_t n_blocks, int32_t n_steps,
   return H3_OK;
 }
 
+size_t h3_dit_forward_tr_workspace_bytes(const h3_shape* shape, const int32_t* tile_start,
+                                         const h3_token_reduction* tr) {
+  Plan pf, pr;
+  if (tr_plans(shape, tile_start, tr, pf, pr) != H3_OK) return 0;
+  return tr_layout(pf, pr).total;
+}
+
+int h3_dit_forward_tr(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_start,
+                      const h3_token_reduction* tr, const h3_block_weights* blocks,
+                      const h3_head_weights* heads, const float* mod, const float* mod_final,
+                      const float* rope, const h3_bf16* x_in, float* vel_video,
+                      float* vel_audio, void* ws, size_t ws_bytes, void* stream) {
+  Plan pf, pr;
+  int rc = tr_plans(shape, tile_start, tr, pf, pr);
+  if (rc) return rc;
+  const TrLayout tl = tr_layout(pf, pr);
+  if (!ws) return fail(H3_EINVAL, "workspace is NULL");
+  if (((uintptr_t)ws & 255) != 0) return fail(H3_EINVAL, "workspace must be 256-byte aligned");
+  if (ws_bytes < tl.total)
+    return fail(H3_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, tl.total);
+  if ((rc = check_dit_args(pf, n_blocks, blocks, heads))) return rc;
+  const int r0 = tr->reduce_at, r1 = tr->restore_at;
+  if (r0 < 0 || r0 > r1 || r1 > n_blocks)
+    return fail(H3_EINVAL, "need 0 <= reduce_at <= restore_at <= n_blocks");
+  if (r0 < r1 && !tr->pairs) return fail(H3_EINVAL, "pairs is NULL");
+  if ((n_blocks > 0 && !mod) || !mod_final || !x_in)
+    return fail(H3_EINVAL, "mod, mod_final and x_in are required");
+  if ((pf.s.n_video > 0 && !vel_video) || (pf.s.n_audio > 0 && !vel_audio))
+    return fail(H3_EINVAL, "velocity outputs are required");
+  if (!aligned16(x_in) || (mod && !aligned16(mod)) || !aligned16(mod_final) ||
+      (rope && !aligned16(rope)) || (tr->rope && !aligned16(tr->rope)))
+    return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const size_t mstride = (size_t)3 * 6 * pf.H;
+  bf16_t* orig = at<bf16_t>(ws, tl.orig);
+  bf16_t* red = at<bf16_t>(ws, tl.red);
+  bf16_t* full = at<bf16_t>(ws, tl.full);
+  TokenArgs ta{};
+  ta.pairs = tr->pairs;
+  ta.P = pf.P;
+  ta.V = pf.s.n_video;
+  ta.Vr = pr.s.n_video;
+  ta.H = pf.H;
+  // full resolution up to reduce_at (blocks alternate between the residual
+  // buffers of the full plan)
+  if ((rc = upload_tables(pf, ws, st))) return rc;
+  const bf16_t* x = x_in;
+  // (each block writes the residual buffer its input is not in)
+  auto next = [&](const Plan& p, const bf16_t* in) {
+    bf16_t* xa = at<bf16_t>(ws, p.lay.xa);
+    return in == xa ? at<bf16_t>(ws, p.lay.xb) : xa;
+  };
+  for (int l = 0; l < r0; ++l) {
+    bf16_t* xo = next(pf, x);
+    if ((rc = run_block(pf, ws, &blocks[l], mod + l * mstride, rope, x, xo, st))) return rc;
+    x = xo;
+  }
+  if (r0 < r1) {
+    ta.x = x;
+    ta.red = red;
+    ta.orig = orig;
+    prof_begin(H3_K_TOKENS, st);
+    H3_TRY(launch_token_pool(ta, st));
+    prof_end(H3_K_TOKENS, st);
+    if ((rc = upload_tables(pr, ws, st))) return rc;
+    x = red;
+    for (int l = r0; l < r1; ++l) {
+      bf16_t* xo = next(pr, x);
+      if ((rc = run_block(pr, ws, &blocks[l], mod + l * mstride, tr->rope, x, xo, st))) return rc;
+      x = xo;
+    }
+    ta.cur = x;
+    ta.out = full;
+    prof_begin(H3_K_TOKENS, st);
+    H3_TRY(launch_token_restore(ta, st));
+    prof_end(H3_K_TOKENS, st);
+    if ((rc = upload_tables(pf, ws, st))) return rc;
+    x = full;
+  }
+  for (int l = r1; l < n_blocks; ++l) {
+    bf16_t* xo = next(pf, x);
+    if ((rc = run_block(pf, ws, &blocks[l], mod + l * mstride, rope, x, xo, st))) return rc;
+    x = xo;
+  }
+  return run_dit(pf, ws, 0, blocks, heads, mod, mod_final, rope, x, vel_video, vel_audio, st);
+}
+
 int h3_routed_attn(const h3_shape* shape, const int32_t* tile_start, const h3_bf16* q,
                    const h3_bf16* k, const h3_bf16* v, const h3_bf16* gate, h3_bf16* out,
                    int32_t* sel, float* scores, void* ws, size_t ws_bytes, void* stream) {
@@ -770,7 +897,7 @@ int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms) {
 const char* h3_prof_kernel_name(int32_t cls) {
   static const char* names[H3_K_COUNT] = {"modnorm", "gemm_qkv", "heads", "route", "attn",
                                           "gemm_o", "gemm_fc1", "gemm_fc2", "final", "tables",
-                                          "rows_in", "time", "euler"};
+                                          "rows_in", "time", "euler", "tokens"};
   return (cls >= 0 && cls < H3_K_COUNT) ? names[cls] : "";
 }
 

@@ -122,6 +122,19 @@ struct TimeGemvArgs {
 hipError_t launch_time_gemv(const TimeGemvArgs& a, hipStream_t s);
 hipError_t launch_euler(float* x, const float* v, size_t n, double dsigma, hipStream_t s);
 
+// ---- token reduction ------------------------------------------------------------
+struct TokenArgs {
+  const bf16_t* x;     // pool: the full stream [P + V][H]
+  bf16_t* red;         // pool: out, the pooled stream [P + Vr][H]; restore: the pooled values kept (base)
+  bf16_t* orig;        // pool: out, the video rows kept [V][H]; restore: in
+  const bf16_t* cur;   // restore: the pooled stream after the reduced blocks [P + Vr][H]
+  bf16_t* out;         // restore: out, the full stream [P + V][H]
+  const int* pairs;    // [Vr][2] full video rows of each pooled token (second -1: single)
+  int P, V, Vr, H;
+};
+hipError_t launch_token_pool(const TokenArgs& a, hipStream_t s);
+hipError_t launch_token_restore(const TokenArgs& a, hipStream_t s);
+
 // ---- small table upload through kernel arguments ------------------------------
 hipError_t launch_poke(int* dst, const int* src, int n, hipStream_t s);
 

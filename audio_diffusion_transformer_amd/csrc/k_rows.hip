@@ -202,7 +202,118 @@ __global__ __launch_bounds__(256) void k_euler(float* __restrict__ x, const floa
   if (i < n) x[i] = (float)((double)x[i] + dsigma * (double)v[i]);
 }
 
+// ---- token reduction ---------------------------------------------------------
+//
+// h3.c README, implementation notes (--token-reduction): after a given block
+// horizontally adjacent video tokens are pooled into one, text and audio rows
+// pass as they are, the full-resolution state is kept; at the restore block
+// each token returns as its kept value plus its pair's update.
+//   pool:    red[r] = bf((x[a] + x[b]) / 2), or x[a] for a single token; orig = x (video rows)
+//   restore: out[i] = bf(orig[i] + (cur[r] - base[r])) for both tokens of pair r,
+//            cur[r] for a single token; prefix rows take cur
+// The sums are formed in fp64 (exact for bf16 operands) and rounded once to
+// bf16 through a round-to-odd step to fp32 (exact round-to-nearest-even).
+// One wave per reduced row, 16-byte vectors; pair indices outside [0, V) are
+// skipped.
+
+__device__ __forceinline__ uint32_t pack2_f64(double a, double b) {
+  float ta = __double2float_rz(a), tb = __double2float_rz(b);
+  if ((double)ta != a) ta = __uint_as_float(__float_as_uint(ta) | 1u);  // round to odd
+  if ((double)tb != b) tb = __uint_as_float(__float_as_uint(tb) | 1u);
+  return pack2(ta, tb);
+}
+
+__global__ __launch_bounds__(256) void k_token_pool(TokenArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);  // reduced-stream row
+  if (r >= a.P + a.Vr) return;
+  const int nv = a.H / 8;
+  if (r < a.P) {  // prefix row: as it is
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.x + (size_t)r * a.H);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.red + (size_t)r * a.H);
+    for (int c = lane; c < nv; c += 64) dst[c] = src[c];
+    return;
+  }
+  const int ia = a.pairs[2 * (r - a.P)], ib = a.pairs[2 * (r - a.P) + 1];
+  if (ia < 0 || ia >= a.V || ib >= a.V) return;
+  const u32x4_t* xa = reinterpret_cast<const u32x4_t*>(a.x + (size_t)(a.P + ia) * a.H);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.red + (size_t)r * a.H);
+  u32x4_t* oa = reinterpret_cast<u32x4_t*>(a.orig + (size_t)ia * a.H);
+  if (ib < 0) {
+    for (int c = lane; c < nv; c += 64) {
+      const u32x4_t v = xa[c];
+      dst[c] = v;
+      oa[c] = v;
+    }
+    return;
+  }
+  const u32x4_t* xb = reinterpret_cast<const u32x4_t*>(a.x + (size_t)(a.P + ib) * a.H);
+  u32x4_t* ob = reinterpret_cast<u32x4_t*>(a.orig + (size_t)ib * a.H);
+  for (int c = lane; c < nv; c += 64) {
+    const u32x4_t u = xa[c], v = xb[c];
+    u32x4_t w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      w[t] = pack2_f64(((double)bflo(u[t]) + (double)bflo(v[t])) * 0.5,
+                       ((double)bfhi(u[t]) + (double)bfhi(v[t])) * 0.5);
+    dst[c] = w;
+    oa[c] = u;
+    ob[c] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_token_restore(TokenArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= a.P + a.Vr) return;
+  const int nv = a.H / 8;
+  const u32x4_t* cur = reinterpret_cast<const u32x4_t*>(a.cur + (size_t)r * a.H);
+  if (r < a.P) {
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.out + (size_t)r * a.H);
+    for (int c = lane; c < nv; c += 64) dst[c] = cur[c];
+    return;
+  }
+  const int ia = a.pairs[2 * (r - a.P)], ib = a.pairs[2 * (r - a.P) + 1];
+  if (ia < 0 || ia >= a.V || ib >= a.V) return;
+  u32x4_t* da = reinterpret_cast<u32x4_t*>(a.out + (size_t)(a.P + ia) * a.H);
+  if (ib < 0) {
+    for (int c = lane; c < nv; c += 64) da[c] = cur[c];
+    return;
+  }
+  const u32x4_t* base = reinterpret_cast<const u32x4_t*>(a.red + (size_t)r * a.H);
+  const u32x4_t* oa = reinterpret_cast<const u32x4_t*>(a.orig + (size_t)ia * a.H);
+  const u32x4_t* ob = reinterpret_cast<const u32x4_t*>(a.orig + (size_t)ib * a.H);
+  u32x4_t* db = reinterpret_cast<u32x4_t*>(a.out + (size_t)(a.P + ib) * a.H);
+  for (int c = lane; c < nv; c += 64) {
+    const u32x4_t cu = cur[c], ba = base[c], u = oa[c], v = ob[c];
+    u32x4_t wa, wb;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const double d0 = (double)bflo(cu[t]) - (double)bflo(ba[t]);
+      const double d1 = (double)bfhi(cu[t]) - (double)bfhi(ba[t]);
+      wa[t] = pack2_f64((double)bflo(u[t]) + d0, (double)bfhi(u[t]) + d1);
+      wb[t] = pack2_f64((double)bflo(v[t]) + d0, (double)bfhi(v[t]) + d1);
+    }
+    da[c] = wa;
+    db[c] = wb;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_token_pool(const TokenArgs& a, hipStream_t s) {
+  const int rows = a.P + a.Vr;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_token_pool, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_restore(const TokenArgs& a, hipStream_t s) {
+  const int rows = a.P + a.Vr;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_token_restore, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_rows_in(const RowsInArgs& a, hipStream_t s) {
   const int nmax = a.n_text > a.n_audio ? (a.n_text > a.n_video ? a.n_text : a.n_video)

@@ -241,6 +241,43 @@ int h3_denoise(const h3_shape* shape, int32_t n_blocks, int32_t n_steps,
                const h3_bf16* text_rows, float* video_latent, float* audio_latent, void* ws,
                size_t ws_bytes, void* stream);
 
+/* Token reduction (h3.c README, implementation notes: --token-reduction):
+ * blocks [reduce_at, restore_at) run on a pooled stream in which pairs of
+ * horizontally adjacent video tokens are one token; text and audio rows pass
+ * as they are.  At reduce_at the pooled token of pair (a, b) is
+ * bf((x[a] + x[b]) / 2) (x[a] for a single token) and the full stream is
+ * kept; at restore_at each token of a pair returns as
+ * bf(kept + (pooled now - pooled at reduce_at)), a single token as its
+ * pooled value, and the remaining blocks run at full resolution.
+ *   reduced:    the pooled stream's shape (n_video = number of pooled tokens,
+ *               n_tiles / n_prefix_tiles of its tile map; every other field as
+ *               in the full shape)
+ *   tile_start: HOST [reduced->n_tiles + 1], its tile map
+ *   pairs:      DEVICE int32 [reduced->n_video][2]: the full video rows (0-based
+ *               within the video segment) of each pooled token, in the pooled
+ *               stream's row order; second entry -1 for a single token.
+ *               Entries outside [0, n_video) are skipped by the kernels.
+ *   rope:       DEVICE fp32 [reduced rows][d/2][2] or NULL: the pooled stream's
+ *               rotary table
+ *   0 <= reduce_at <= restore_at <= n_blocks (equal: no reduction). */
+typedef struct {
+  const h3_shape* reduced;
+  const int32_t* tile_start;
+  const int32_t* pairs;
+  const float* rope;
+  int32_t reduce_at, restore_at;
+} h3_token_reduction;
+
+/* h3_dit_forward with token reduction.  Workspace:
+ * h3_dit_forward_tr_workspace_bytes(shape, tile_start, tr) bytes. */
+size_t h3_dit_forward_tr_workspace_bytes(const h3_shape* shape, const int32_t* tile_start,
+                                         const h3_token_reduction* tr);
+int h3_dit_forward_tr(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_start,
+                      const h3_token_reduction* tr, const h3_block_weights* blocks,
+                      const h3_head_weights* heads, const float* mod, const float* mod_final,
+                      const float* rope, const h3_bf16* x_in, float* vel_video,
+                      float* vel_audio, void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel-time accounting for diagnostics: while enabled, each kernel launch
  * of the library is bracketed by HIP events on its stream.  h3_prof_read
  * synchronizes those events and returns, for kernel class `cls` (H3_K_*),
@@ -248,7 +285,7 @@ int h3_denoise(const h3_shape* shape, int32_t n_blocks, int32_t n_steps,
  * the events it has read.  Not thread-safe; for benchmarks. */
 enum { H3_K_NORM = 0, H3_K_GEMM_QKV, H3_K_HEADS, H3_K_ROUTE, H3_K_ATTN, H3_K_GEMM_O,
        H3_K_GEMM_FC1, H3_K_GEMM_FC2, H3_K_FINAL, H3_K_TABLES, H3_K_ROWS_IN, H3_K_TIME,
-       H3_K_EULER, H3_K_COUNT };
+       H3_K_EULER, H3_K_TOKENS, H3_K_COUNT };
 int h3_prof_enable(int on);
 int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms);
 const char* h3_prof_kernel_name(int32_t cls);

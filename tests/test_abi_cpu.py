@@ -170,3 +170,34 @@ def test_denoise_entry_points_validate_before_launch(lib):
                         ctypes.byref(tw2), sig2, None, None, None, None, ctypes.c_void_p(256),
                         1 << 40, None)
     assert rc == B.H3_EINVAL and "head widths" in B.last_error()
+
+
+def test_token_reduction_validates_before_launch(lib):
+    sh = S.FASTH3_TINY
+    shape, ts = _shape(sh)
+    tp = ts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    red, pairs, first = S.token_pairs(sh)
+    rshape, rts = _shape(red)
+    tr = B.TokenReduction(rshape, rts, None, None, 1, 3)
+    n = lib.h3_dit_forward_tr_workspace_bytes(ctypes.byref(shape), tp, ctypes.byref(tr.c))
+    assert n > lib.h3_workspace_bytes(ctypes.byref(shape), tp, B.H3_WS_DIT)
+    hw = B.H3HeadWeights(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                         ctypes.c_void_p(256), 96, 32)
+    w = (B.H3BlockWeights * 4)(*[B.H3BlockWeights(*[ctypes.c_void_p(256)] * 10)] * 4)
+
+    def call(trc, L=4):
+        return lib.h3_dit_forward_tr(ctypes.byref(shape), L, tp, ctypes.byref(trc), w,
+                                     ctypes.byref(hw), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                     None, ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                     ctypes.c_void_p(256), ctypes.c_void_p(256), 1 << 40, None)
+    assert call(tr.c) == B.H3_EINVAL and "pairs" in B.last_error()
+    bad = B.TokenReduction(rshape, rts, None, None, 3, 1)
+    assert call(bad.c) == B.H3_EINVAL and "reduce_at" in B.last_error()
+    bad = B.TokenReduction(rshape, rts, None, None, 1, 5)
+    assert call(bad.c) == B.H3_EINVAL
+    rs2 = B.H3Shape.from_buffer_copy(rshape)
+    rs2.hidden = 512
+    bad = B.TokenReduction(rs2, rts, None, None, 1, 3)
+    assert call(bad.c) == B.H3_EINVAL and "reduced shape" in B.last_error()
+    assert lib.h3_dit_forward_tr(ctypes.byref(shape), 4, tp, None, w, ctypes.byref(hw), None,
+                                 None, None, None, None, None, None, 0, None) == B.H3_EINVAL
