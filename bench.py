@@ -35,6 +35,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 N_BLOCKS = 50
 N_PASSES = 8                # denoising passes of --denoise (the pages' 8-step schedule)
+TR_REDUCE_AT, TR_RESTORE_AT = 4, 40  # token reduction after block 3, restore before block 40
 PAGES_FASTH3_S = 10.1       # the pages' 50-block FastH3 forward, median of steps 2-8, M5 Ultra
 
 
@@ -50,6 +51,9 @@ def parse():
                     help="full: the default 50-block forward (hidden 5120, GELU); fasth3: the "
                          "pages' own block and geometry (hidden 5376, 56x128 heads, SwiGLU "
                          "14336, routing gate, cube tiles, top-k 56)")
+    ap.add_argument("--token-reduction", action="store_true",
+                    help="with --workload fasth3: blocks 4 .. 39 on the pooled stream (pairs of "
+                         "horizontally adjacent video tokens), as in the pages' early passes")
     ap.add_argument("--denoise", action="store_true",
                     help="time h3_denoise instead: 8 passes of rows in, modulation tables, "
                          "the 50-block forward and heads, and the Euler step, per timed step")
@@ -370,8 +374,24 @@ def main():
     torch.cuda.synchronize()
     print("setup done", file=sys.stderr, flush=True)
 
+    tr = None
+    if args.token_reduction:
+        if not sh.cube:
+            raise SystemExit("--token-reduction needs a video grid: use --workload fasth3")
+        red, pairs, first = S.token_pairs(sh)
+        rts, rnpt = S.tile_map(red)
+        tr = B.TokenReduction(B.make_shape(red, rts, rnpt), rts, T.to_dev(pairs),
+                              T.to_dev(S.rope_tables(red, first)), min(TR_REDUCE_AT, L),
+                              min(TR_RESTORE_AT, L))
+        ws = T.workspace(B.dit_forward_tr_workspace_bytes(shape, ts, tr))
+
     def forward(s):
-        B.dit_forward(shape, ts, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws, stream=stream)
+        if tr is None:
+            B.dit_forward(shape, ts, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws,
+                          stream=stream)
+        else:
+            B.dit_forward_tr(shape, ts, tr, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws,
+                             stream=stream)
 
     for s in range(args.warmup):
         forward(s)
@@ -397,6 +417,11 @@ def main():
 
     # ---- per-kernel roofline from the events of the timed region ----
     work = kernel_work(sh, ts, npt, attention_keys(sh, ts, npt))
+    if tr is not None:  # mean work per launch over full-resolution and pooled blocks
+        nr = tr.c.restore_at - tr.c.reduce_at
+        nf = L - nr
+        wr = kernel_work(red, rts, rnpt, attention_keys(red, rts, rnpt))
+        work = {k: (v[0], (nf * v[1] + nr * wr[k][1]) / max(L, 1)) for k, v in work.items()}
     kernels = {}
     for name, (n, ms) in kern.items():
         if n == 0:
@@ -434,7 +459,8 @@ def main():
     line = {
         "metric": ("s per 50-block DiT forward at 15,435 rows; GEMM/attn % of bf16 MFMA peak"
                    if args.workload == "full" else
-                   "s per 50-block FastH3 forward at 15,435 rows (the pages' block and geometry)"),
+                   "s per 50-block FastH3 forward at 15,435 rows (the pages' block and geometry)"
+                   + (", token reduction in blocks 4-39" if tr is not None else "")),
         "value": round(ms_per_step / 1e3, 5),
         "unit": "s",
         "n_gpus": 1,
@@ -446,7 +472,7 @@ def main():
         # the pages time this same forward (FastH3 geometry, 50 blocks) at 10.1 s
         # on an Apple M5 Ultra: another machine, a ratio for context only
         "vs_baseline": (round(ms_per_step / 1e3 / PAGES_FASTH3_S, 4)
-                        if args.workload == "fasth3" else None),
+                        if args.workload == "fasth3" and tr is None else None),
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": (f"{L}-block H3-style DiT forward, 15,435 rows (512 text / 543 "
