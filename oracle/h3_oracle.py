@@ -334,7 +334,7 @@ def attention(q, k, v, tile_start, n_prefix_tiles, n_prefix_rows, rt, use_pooled
 
 
 def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=None,
-                  timings=None):
+                  timings=None, qw=None, fc2_group=0):
     """One DiT block, steps in the order of TensorFold PR #949 "What it adds"
     (block.zig) with the GELU MLP of the workload description:
 
@@ -361,6 +361,11 @@ def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=N
     computed (q, k, v and routing always cover all rows).
     timings: None, or a dict that receives the wall time of the all-row part
     ("all_rows") and of the per-row part ("per_row").
+    qw: None, or the int8 codes and scales of the four products
+    (quantize_block_int8): each product then quantizes its bf16 input per row
+    (the FC2 input per group of fc2_group columns if fc2_group > 0) and
+    computes linear_int8 (h3.c README: the int8 QKV, attention-output and MLP
+    products); everything else is unchanged.
     Returns a dict of float64 intermediates (bf16 values where rounded)."""
     t0 = time.perf_counter()
     mlp = int(getattr(sh, "mlp", 0))
@@ -374,8 +379,14 @@ def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=N
     eps = sh.norm_eps
     f = {k_: bf16_to_f64(v_) for k_, v_ in w.items()}
 
+    def lin(a_, name, group=0):
+        if qw is None:
+            return linear(a_, f["w_" + name], f["b_" + name])
+        qa, sa = quantize_int8(a_, group)
+        return linear_int8(qa, sa, qw["w_" + name], qw["s_" + name], f["b_" + name], group)
+
     n1 = modulated_rmsnorm(x, shift1, scale1, seg, eps)
-    y = round_bf16(linear(n1, f["w_qkv"], f["b_qkv"]))
+    y = round_bf16(lin(n1, "qkv"))
     parts = split_qkv(y, sh.n_heads, sh.head_dim, 4 if use_gate else 3)
     q, k, v = parts[:3]
     g = parts[3] if use_gate else None
@@ -386,15 +397,15 @@ def block_forward(sh, tile_start, n_prefix_tiles, w, mod, rope, x_in, out_rows=N
     t1 = time.perf_counter()
     a = round_bf16(attention(qt, kt, v, ts, n_prefix_tiles, P, rt, bool(sh.pooled), rows, g))
     sr = seg[rows]
-    o = round_bf16(linear(a, f["w_o"], f["b_o"]))
+    o = round_bf16(lin(a, "o"))
     x1 = round_bf16(x[rows] + gate1[sr] * o)
     n2 = modulated_rmsnorm(x1, shift2, scale2, sr, eps)
-    z1 = linear(n2, f["w_fc1"], f["b_fc1"])
+    z1 = lin(n2, "fc1")
     if mlp == 1:
         hdn = swiglu_hidden(z1, z1.shape[1] // 2)
     else:
         hdn = round_bf16(gelu(z1))
-    ff = round_bf16(linear(hdn, f["w_fc2"], f["b_fc2"]))
+    ff = round_bf16(lin(hdn, "fc2", fc2_group))
     x2 = round_bf16(x1 + gate2[sr] * ff)
     if timings is not None:
         timings["all_rows"] = t1 - t0
@@ -421,14 +432,17 @@ def final_heads(sh, x, mod_final, head):
     return vel_video, vel_audio
 
 
-def dit_forward(sh, tile_start, n_prefix_tiles, blocks, head, mods, mod_final, rope, x_in):
+def dit_forward(sh, tile_start, n_prefix_tiles, blocks, head, mods, mod_final, rope, x_in,
+                qws=None, fc2_group=0):
     """L blocks, then the final norm and heads (TensorFold PR #949 opening
     summary: 50 blocks denoise one packed sequence).  blocks: list of weight
-    dicts; mods: [L][3][6][H]."""
+    dicts; mods: [L][3][6][H]; qws: None or the blocks' int8 products
+    (quantize_block_int8), see block_forward."""
     x_bits = np.asarray(x_in, dtype=np.uint16)
     x = bf16_to_f64(x_bits)
     for l, w in enumerate(blocks):
-        r = block_forward(sh, tile_start, n_prefix_tiles, w, mods[l], rope, x_bits)
+        r = block_forward(sh, tile_start, n_prefix_tiles, w, mods[l], rope, x_bits,
+                          qw=None if qws is None else qws[l], fc2_group=fc2_group)
         x = r["x2"]
         x_bits = f64_to_bf16_bits(x)
     vv, va = final_heads(sh, x, mod_final, head)
@@ -620,3 +634,59 @@ def dit_forward_reduced(sh, tile_start, n_prefix_tiles, red_sh, red_tile_start, 
         x = token_restore(x, orig, base, pairs, P, sh.n_video)
     vv, va = final_heads(sh, x, mod_final, head)
     return dict(x=x, vel_video=vv, vel_audio=va)
+
+
+# ----------------------------------------------------------------------------
+# int8 products
+# ----------------------------------------------------------------------------
+
+def quantize_int8(x, group=0):
+    """Symmetric int8 codes (h3.c README, implementation notes: the int8 MLP
+    quantizes activations dynamically, per-output-channel weight scales, one
+    scale per 1,024 channels for the FC2 input).  Per row, or per group of
+    `group` consecutive columns: m = max |x|, code = rint(x * (127 / m))
+    clamped to [-127, 127], scale = m / 127, all in fp32 arithmetic (the
+    codes are decisions, taken in the kernels' precision).  A zero group has
+    codes 0 and scale 0.  x: float64 values of bf16 numbers [n][K].
+    Returns (codes int8 [n][K], scales fp32 [n] or [n][K/group])."""
+    xf = np.asarray(x, dtype=np.float32)
+    n, K = xf.shape
+    g = K if group == 0 else group
+    xg = xf.reshape(n, K // g, g)
+    m = np.max(np.abs(xg), axis=2)
+    with np.errstate(divide="ignore"):
+        inv = np.where(m > 0, np.float32(127.0) / m, np.float32(0.0)).astype(np.float32)
+    codes = np.clip(np.rint(xg * inv[:, :, None]), -127, 127).astype(np.int8).reshape(n, K)
+    scale = (m / np.float32(127.0)).astype(np.float32)
+    return codes, (scale[:, 0] if group == 0 else scale)
+
+
+def quantize_weight_int8(w_bits):
+    """Per-output-channel int8 codes of a bf16 weight [out][in] (rows)."""
+    return quantize_int8(bf16_to_f64(w_bits))
+
+
+def linear_int8(qa, sa, qw, sw, b, group=0):
+    """y = sum_k qa qw * sa * sw + b: exact integer sums, then the scales in
+    float64.  With `group`, sa is [n][K/group] and each group's sum takes its
+    own activation scale."""
+    qa64, qw64 = qa.astype(np.int64), qw.astype(np.int64)
+    swf = np.asarray(sw, dtype=np.float64)
+    if group == 0:
+        acc = (qa64 @ qw64.T).astype(np.float64)
+        return acc * np.asarray(sa, dtype=np.float64)[:, None] * swf[None, :] + b
+    n, K = qa.shape
+    y = np.zeros((n, qw.shape[0]))
+    for gi in range(K // group):
+        sl = slice(gi * group, (gi + 1) * group)
+        y += (qa64[:, sl] @ qw64[:, sl].T).astype(np.float64) * \
+            np.asarray(sa, dtype=np.float64)[:, gi:gi + 1]
+    return y * swf[None, :] + b
+
+
+def quantize_block_int8(w):
+    """int8 codes and scales of a block's four weight matrices."""
+    out = {}
+    for name in ("qkv", "o", "fc1", "fc2"):
+        out["w_" + name], out["s_" + name] = quantize_weight_int8(w["w_" + name])
+    return out

@@ -760,3 +760,56 @@ def test_reduced_forward_with_identity_middle_equals_the_outer_blocks():
                         S.rope_tables(sh), x)
     np.testing.assert_array_equal(got["vel_video"], ref["vel_video"])
     np.testing.assert_array_equal(got["vel_audio"], ref["vel_audio"])
+
+
+# ----------------------------------------------------------------------------
+# int8 products
+# ----------------------------------------------------------------------------
+
+def test_quantize_int8_exact_grid_and_ties():
+    # max 127 * 2^-3: scale 2^-3, and multiples of 2^-3 map to exact integer codes
+    x = np.array([[127 / 8, -5 / 8, 0.0, 1 / 8]])
+    q, s = O.quantize_int8(x)
+    assert s[0] == np.float32(0.125)
+    np.testing.assert_array_equal(q, [[127, -5, 0, 1]])
+    # max 127 (inv = 1): 2.5 -> 2 and 3.5 -> 4 (round half to even), -2.5 -> -2
+    q, s = O.quantize_int8(np.array([[127.0, 2.5, 3.5, -2.5]]))
+    np.testing.assert_array_equal(q, [[127, 2, 4, -2]])
+    # a zero row: codes 0, scale 0
+    q, s = O.quantize_int8(np.zeros((1, 4)))
+    assert s[0] == 0 and np.all(q == 0)
+
+
+def test_quantize_int8_groups_are_independent():
+    x = np.array([[1.0, -2.0, 100.0, 50.0]])
+    q, s = O.quantize_int8(x, group=2)
+    np.testing.assert_array_equal(q, [[64, -127, 127, 64]])      # 1 * 127/2 = 63.5 -> 64 (even)
+    np.testing.assert_array_equal(s, np.array([[2.0, 100.0]], np.float32) / np.float32(127))
+
+
+def test_linear_int8_equals_float_product_on_exact_codes():
+    rng = np.random.default_rng(0)
+    qa = rng.integers(-127, 128, (5, 256)).astype(np.int8)
+    qw = rng.integers(-127, 128, (7, 256)).astype(np.int8)
+    sa = np.array([0.5, 0.25, 1.0, 2.0, 0.125], np.float32)
+    sw = np.array([1, 2, 4, 0.5, 0.25, 8, 1], np.float32)
+    b = np.arange(7) * 0.5
+    y = O.linear_int8(qa, sa, qw, sw, b)
+    ref = (qa.astype(np.float64) * sa[:, None]) @ (qw.astype(np.float64) * sw[:, None]).T + b
+    np.testing.assert_array_equal(y, ref)
+    # grouped: one scale per group of 128 columns
+    sg = np.stack([sa, 2 * sa], axis=1)
+    yg = O.linear_int8(qa, sg, qw, sw, b, group=128)
+    ag = qa.astype(np.float64) * np.repeat(sg, 128, axis=1)
+    np.testing.assert_array_equal(yg, ag @ (qw.astype(np.float64) * sw[:, None]).T + b)
+
+
+def test_int8_block_stays_close_to_the_bf16_block():
+    sh, ts, npt, w, mod, rope, x = _tiny_block_inputs()
+    ref = O.block_forward(sh, ts, npt, w, mod, rope, x)
+    q = O.block_forward(sh, ts, npt, w, mod, rope, x, qw=O.quantize_block_int8(w))
+    d, r = q["x2"] - O.bf16_to_f64(x), ref["x2"] - O.bf16_to_f64(x)   # the block's update
+    cos = float(np.sum(d * r) / np.linalg.norm(d) / np.linalg.norm(r))
+    assert cos > 0.99, cos
+    # and the int8 path really differs (it is not the bf16 path)
+    assert not np.array_equal(q["x2"], ref["x2"])
