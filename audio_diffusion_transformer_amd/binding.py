@@ -16,11 +16,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libh3.so")
 
 H3_OK, H3_EINVAL, H3_EWORKSPACE, H3_EHIP, H3_EUNSUPPORTED = 0, -1, -2, -3, -4
-H3_WS_BLOCK, H3_WS_DIT, H3_WS_ATTN = 0, 1, 2
+H3_WS_BLOCK, H3_WS_DIT, H3_WS_ATTN, H3_WS_DIT_I8 = 0, 1, 2, 3
 ABI_VERSION = 3  # must match H3_ABI_VERSION in include/h3.h
 
 KERNEL_CLASSES = ["modnorm", "gemm_qkv", "heads", "route", "attn", "gemm_o", "gemm_fc1",
-                  "gemm_fc2", "final", "tables", "rows_in", "time", "euler", "tokens"]
+                  "gemm_fc2", "final", "tables", "rows_in", "time", "euler", "tokens", "quant"]
 
 _vp = ctypes.c_void_p
 
@@ -55,6 +55,11 @@ class H3TimeWeights(ctypes.Structure):
                                    "w_final", "b_final")]
 
 
+class H3BlockWeightsI8(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w_qkv", "s_qkv", "b_qkv", "q_gain", "k_gain", "w_o", "s_o",
+                                   "b_o", "w_fc1", "s_fc1", "b_fc1", "w_fc2", "s_fc2", "b_fc2")]
+
+
 class H3TokenReduction(ctypes.Structure):
     _fields_ = [("reduced", ctypes.POINTER(H3Shape)), ("tile_start", ctypes.POINTER(ctypes.c_int32)),
                 ("pairs", _vp), ("rope", _vp), ("reduce_at", ctypes.c_int32),
@@ -64,7 +69,8 @@ class H3TokenReduction(ctypes.Structure):
 class H3WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("tables", "norm", "big", "q", "k", "vt", "qbar",
                                                "kbar", "vbar", "scores", "sel", "pooled",
-                                               "attn", "x1", "xa", "xb", "total")] + \
+                                               "attn", "x1", "xa", "xb", "q8", "qscale",
+                                               "total")] + \
                [("padded_rows", ctypes.c_int32), ("n_query_tiles", ctypes.c_int32),
                 ("n_sel", ctypes.c_int32)]
 
@@ -121,6 +127,12 @@ def lib():
                                     ctypes.POINTER(H3TokenReduction),
                                     ctypes.POINTER(H3BlockWeights), ctypes.POINTER(H3HeadWeights),
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.h3_quantize_rows.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+                                   _vp]
+    L.h3_dit_forward_i8.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32, i32p,
+                                    ctypes.POINTER(H3BlockWeightsI8),
+                                    ctypes.POINTER(H3HeadWeights), _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, ctypes.c_size_t, _vp]
     L.h3_prof_enable.argtypes = [ctypes.c_int]
     L.h3_prof_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                ctypes.POINTER(ctypes.c_double)]
@@ -128,6 +140,7 @@ def lib():
     L.h3_prof_kernel_name.restype = ctypes.c_char_p
     for f in (L.h3_workspace_layout, L.h3_block_forward, L.h3_dit_forward, L.h3_routed_attn,
               L.h3_rows_in, L.h3_modulation, L.h3_denoise, L.h3_dit_forward_tr,
+              L.h3_quantize_rows, L.h3_dit_forward_i8,
               L.h3_prof_enable, L.h3_prof_read):
         f.restype = ctypes.c_int
     _lib = L
@@ -321,6 +334,46 @@ def dit_forward_tr(shape, tile_start, tr: TokenReduction, blocks, heads, mod, mo
                                    ctypes.byref(hw), _ptr(mod), _ptr(mod_final), _ptr(rope),
                                    _ptr(x_in), _ptr(vel_video), _ptr(vel_audio), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def quantize_rows(x, q, scale, group=0, stream=None):
+    """int8 codes of the bf16 matrix x [rows][cols] (device tensors)."""
+    rows, cols = x.shape
+    _check(lib().h3_quantize_rows(_ptr(x), rows, cols, group, _ptr(q), _ptr(scale),
+                                  _stream(stream)))
+
+
+def quantize_block(w, stream=None):
+    """int8 codes and row scales of a block's four products: w is a dict of
+    device tensors (bf16 bits); returns the dict of h3_block_weights_i8."""
+    import torch
+    out = {k: w[k] for k in ("b_qkv", "q_gain", "k_gain", "b_o", "b_fc1", "b_fc2")}
+    for n in ("qkv", "o", "fc1", "fc2"):
+        m = w["w_" + n]
+        out["w_" + n] = torch.empty(m.shape, dtype=torch.int8, device=m.device)
+        out["s_" + n] = torch.empty(m.shape[0], dtype=torch.float32, device=m.device)
+        quantize_rows(m, out["w_" + n], out["s_" + n], 0, stream)
+    return out
+
+
+def block_weights_i8_struct(w):
+    return H3BlockWeightsI8(*[_ptr(w[n]) for n, _ in H3BlockWeightsI8._fields_])
+
+
+def dit_forward_i8(shape, tile_start, blocks, heads, mod, mod_final, rope, x_in, vel_video,
+                   vel_audio, ws, stream=None):
+    """blocks: list of int8 weight dicts (quantize_block) or a prebuilt array."""
+    ts, tp = _tiles(tile_start)
+    if isinstance(blocks, (list, tuple)):
+        arr = (H3BlockWeightsI8 * max(len(blocks), 1))(*[block_weights_i8_struct(b) for b in blocks])
+        n = len(blocks)
+    else:
+        arr, n = blocks, len(blocks)
+    hw = head_weights_struct(heads) if isinstance(heads, dict) else heads
+    _check(lib().h3_dit_forward_i8(ctypes.byref(shape), n, tp, arr, ctypes.byref(hw), _ptr(mod),
+                                   _ptr(mod_final), _ptr(rope), _ptr(x_in), _ptr(vel_video),
+                                   _ptr(vel_audio), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
 
 
 def prof_enable(on=True):

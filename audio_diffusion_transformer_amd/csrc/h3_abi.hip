@@ -56,7 +56,8 @@ struct Plan {
 int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) {
   if (!s) return fail(H3_EINVAL, "shape is NULL");
   if (!tile_start) return fail(H3_EINVAL, "tile_start is NULL");
-  if (which < H3_WS_BLOCK || which > H3_WS_ATTN) return fail(H3_EINVAL, "bad workspace kind %d", which);
+  if (which < H3_WS_BLOCK || which > H3_WS_DIT_I8)
+    return fail(H3_EINVAL, "bad workspace kind %d", which);
   p.s = *s;
   if (s->n_text < 0 || s->n_audio < 0 || s->n_video < 0)
     return fail(H3_EINVAL, "negative row count");
@@ -85,6 +86,11 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
     if (!gemm_shape_ok(p.R, p.parts * p.A, p.H) || !gemm_shape_ok(p.R, p.H, p.A) ||
         !gemm_shape_ok(p.R, p.F1, p.H) || !gemm_shape_ok(p.R, p.H, s->ffn))
       return fail(H3_EUNSUPPORTED, "rows x width too large for the GEMM (R*F must stay below 2^31)");
+    if (which == H3_WS_DIT_I8 &&
+        (!gemm_i8_shape_ok(p.R, p.parts * p.A, p.H) || !gemm_i8_shape_ok(p.R, p.H, p.A) ||
+         !gemm_i8_shape_ok(p.R, p.F1, p.H) || !gemm_i8_shape_ok(p.R, p.H, s->ffn)))
+      return fail(H3_EUNSUPPORTED, "int8 products need hidden, attention and FFN widths that are "
+                                   "multiples of 256");
   }
   if (!(s->norm_eps >= 0.f)) return fail(H3_EINVAL, "norm_eps must be >= 0");
   p.nT = s->n_tiles;
@@ -168,9 +174,15 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
     L.attn = take(R * A * bf);
     L.x1 = take(R * H * bf);
   }
-  if (which == H3_WS_DIT) {
+  if (which == H3_WS_DIT || which == H3_WS_DIT_I8) {
     L.xa = take(R * H * bf);
     L.xb = take(R * H * bf);
+  }
+  if (which == H3_WS_DIT_I8) {
+    size_t w8 = H > A ? H : A;
+    if ((size_t)p.F > w8) w8 = p.F;
+    L.q8 = take(R * w8);
+    L.qscale = take(R * f4);
   }
   L.total = off;
   L.padded_rows = p.Rp;
@@ -370,6 +382,110 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
   e.n_prefix = np_;
   prof_begin(H3_K_GEMM_FC2, st);
   H3_TRY(launch_gemm(EPI_BIAS_RESGATE, big, w->w_fc2, R, H, F, e, st));
+  prof_end(H3_K_GEMM_FC2, st);
+  return H3_OK;
+}
+
+int check_block_weights_i8(const h3_block_weights_i8* w, int l) {
+  if (!w) return fail(H3_EINVAL, "block %d weights NULL", l);
+  const void* ptrs[] = {w->w_qkv, w->s_qkv, w->b_qkv, w->q_gain, w->k_gain, w->w_o, w->s_o,
+                        w->b_o, w->w_fc1, w->s_fc1, w->b_fc1, w->w_fc2, w->s_fc2, w->b_fc2};
+  for (const void* q : ptrs) {
+    if (!q) return fail(H3_EINVAL, "block %d: a weight pointer is NULL", l);
+    if (!aligned16(q)) return fail(H3_EINVAL, "block %d: a weight pointer is not 16-byte aligned", l);
+  }
+  return H3_OK;
+}
+
+// The block with int8 products: the norms emit row codes, the attention output
+// and the MLP hidden are quantized per row before their products.
+int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const float* mod,
+                 const float* rope, const bf16_t* x_in, bf16_t* x_out, hipStream_t st) {
+  const int R = p.R, H = p.H, F = p.F, A = p.A;
+  const int nt = p.s.n_text, np_ = p.P;
+  bf16_t* big = at<bf16_t>(ws, p.lay.big);
+  bf16_t* attn = at<bf16_t>(ws, p.lay.attn);
+  bf16_t* x1 = at<bf16_t>(ws, p.lay.x1);
+  int8_t* q8 = at<int8_t>(ws, p.lay.q8);
+  float* qs = at<float>(ws, p.lay.qscale);
+  const int ms = 6 * H;
+
+  prof_begin(H3_K_NORM, st);
+  H3_TRY(launch_modnorm_q(x_in, mod + 0 * H, mod + 1 * H, ms, R, H, nt, np_, p.s.norm_eps, q8, qs,
+                          nullptr, st));
+  prof_end(H3_K_NORM, st);
+
+  GemmEpi e{};
+  e.bias = w->b_qkv;
+  e.out = big;
+  e.n_text = nt;
+  e.n_prefix = np_;
+  e.a_scale = qs;
+  e.b_scale = w->s_qkv;
+  prof_begin(H3_K_GEMM_QKV, st);
+  H3_TRY(launch_gemm_i8(EPI_BIAS, q8, w->w_qkv, R, p.parts * A, H, e, st));
+  prof_end(H3_K_GEMM_QKV, st);
+
+  HeadsArgs ha = heads_args(p, ws);
+  ha.y = big;
+  ha.q_gain = w->q_gain;
+  ha.k_gain = w->k_gain;
+  ha.rope = rope;
+  prof_begin(H3_K_HEADS, st);
+  H3_TRY(launch_heads(HEADS_QKV, p.D, ha, st));
+  prof_end(H3_K_HEADS, st);
+
+  const bf16_t* gate = p.s.gate ? big + 3 * p.D : nullptr;
+  int rc = run_attention(p, ws, nullptr, nullptr, attn, gate, p.parts * A, p.parts * p.D, st);
+  if (rc) return rc;
+
+  prof_begin(H3_K_QUANT, st);
+  H3_TRY(launch_quant_rows(attn, R, A, A, q8, qs, st));
+  prof_end(H3_K_QUANT, st);
+  e = GemmEpi{};
+  e.bias = w->b_o;
+  e.out = x1;
+  e.res = x_in;
+  e.gate = mod + 2 * H;
+  e.gate_seg_stride = ms;
+  e.n_text = nt;
+  e.n_prefix = np_;
+  e.a_scale = qs;
+  e.b_scale = w->s_o;
+  prof_begin(H3_K_GEMM_O, st);
+  H3_TRY(launch_gemm_i8(EPI_BIAS_RESGATE, q8, w->w_o, R, H, A, e, st));
+  prof_end(H3_K_GEMM_O, st);
+
+  prof_begin(H3_K_NORM, st);
+  H3_TRY(launch_modnorm_q(x1, mod + 3 * H, mod + 4 * H, ms, R, H, nt, np_, p.s.norm_eps, q8, qs,
+                          nullptr, st));
+  prof_end(H3_K_NORM, st);
+
+  e = GemmEpi{};
+  e.bias = w->b_fc1;
+  e.out = big;
+  e.a_scale = qs;
+  e.b_scale = w->s_fc1;
+  prof_begin(H3_K_GEMM_FC1, st);
+  H3_TRY(launch_gemm_i8(p.s.mlp == H3_MLP_SWIGLU ? EPI_BIAS_SWIGLU : EPI_BIAS_GELU, q8, w->w_fc1,
+                        R, p.F1, H, e, st));
+  prof_end(H3_K_GEMM_FC1, st);
+
+  prof_begin(H3_K_QUANT, st);
+  H3_TRY(launch_quant_rows(big, R, F, F, q8, qs, st));
+  prof_end(H3_K_QUANT, st);
+  e = GemmEpi{};
+  e.bias = w->b_fc2;
+  e.out = x_out;
+  e.res = x1;
+  e.gate = mod + 5 * H;
+  e.gate_seg_stride = ms;
+  e.n_text = nt;
+  e.n_prefix = np_;
+  e.a_scale = qs;
+  e.b_scale = w->s_fc2;
+  prof_begin(H3_K_GEMM_FC2, st);
+  H3_TRY(launch_gemm_i8(EPI_BIAS_RESGATE, q8, w->w_fc2, R, H, F, e, st));
   prof_end(H3_K_GEMM_FC2, st);
   return H3_OK;
 }
@@ -843,6 +959,56 @@ int h3_dit_forward_tr(const h3_shape* shape, int32_t n_blocks, const int32_t* ti
   return run_dit(pf, ws, 0, blocks, heads, mod, mod_final, rope, x, vel_video, vel_audio, st);
 }
 
+int h3_quantize_rows(const h3_bf16* x, int32_t rows, int32_t cols, int32_t group, int8_t* q,
+                     float* scale, void* stream) {
+  if (rows < 0) return fail(H3_EINVAL, "rows < 0");
+  const int G = group == 0 ? cols : group;
+  if (!quant_shape_ok(cols, G))
+    return fail(H3_EINVAL, "cols %d and group %d: multiples of 8, group <= 32768 dividing cols",
+                cols, group);
+  if (rows > 0 && (!x || !q || !scale)) return fail(H3_EINVAL, "x, q and scale are required");
+  if ((x && !aligned16(x)) || (q && ((uintptr_t)q & 7) != 0))
+    return fail(H3_EINVAL, "x must be 16-byte and q 8-byte aligned");
+  prof_begin(H3_K_QUANT, (hipStream_t)stream);
+  H3_TRY(launch_quant_rows(x, rows, cols, G, q, scale, (hipStream_t)stream));
+  prof_end(H3_K_QUANT, (hipStream_t)stream);
+  return H3_OK;
+}
+
+int h3_dit_forward_i8(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_start,
+                      const h3_block_weights_i8* blocks, const h3_head_weights* heads,
+                      const float* mod, const float* mod_final, const float* rope,
+                      const h3_bf16* x_in, float* vel_video, float* vel_audio, void* ws,
+                      size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(shape, tile_start, H3_WS_DIT_I8, p);
+  if (rc) return rc;
+  if ((rc = check_ws(p, ws, ws_bytes))) return rc;
+  if (n_blocks < 0) return fail(H3_EINVAL, "n_blocks < 0");
+  if (n_blocks > 0 && !blocks) return fail(H3_EINVAL, "blocks is NULL");
+  for (int l = 0; l < n_blocks; ++l)
+    if ((rc = check_block_weights_i8(&blocks[l], l))) return rc;
+  if ((rc = check_dit_args(p, 0, nullptr, heads))) return rc;
+  if ((n_blocks > 0 && !mod) || !mod_final || !x_in)
+    return fail(H3_EINVAL, "mod, mod_final and x_in are required");
+  if ((p.s.n_video > 0 && !vel_video) || (p.s.n_audio > 0 && !vel_audio))
+    return fail(H3_EINVAL, "velocity outputs are required");
+  if (!aligned16(x_in) || (mod && !aligned16(mod)) || !aligned16(mod_final) ||
+      (rope && !aligned16(rope)))
+    return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = upload_tables(p, ws, st))) return rc;
+  const bf16_t* x = x_in;
+  const size_t mstride = (size_t)3 * 6 * p.H;
+  for (int l = 0; l < n_blocks; ++l) {
+    bf16_t* xa = at<bf16_t>(ws, p.lay.xa);
+    bf16_t* xo = x == xa ? at<bf16_t>(ws, p.lay.xb) : xa;
+    if ((rc = run_block_i8(p, ws, &blocks[l], mod + l * mstride, rope, x, xo, st))) return rc;
+    x = xo;
+  }
+  return run_dit(p, ws, 0, nullptr, heads, mod, mod_final, rope, x, vel_video, vel_audio, st);
+}
+
 int h3_routed_attn(const h3_shape* shape, const int32_t* tile_start, const h3_bf16* q,
                    const h3_bf16* k, const h3_bf16* v, const h3_bf16* gate, h3_bf16* out,
                    int32_t* sel, float* scores, void* ws, size_t ws_bytes, void* stream) {
@@ -897,7 +1063,7 @@ int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms) {
 const char* h3_prof_kernel_name(int32_t cls) {
   static const char* names[H3_K_COUNT] = {"modnorm", "gemm_qkv", "heads", "route", "attn",
                                           "gemm_o", "gemm_fc1", "gemm_fc2", "final", "tables",
-                                          "rows_in", "time", "euler", "tokens"};
+                                          "rows_in", "time", "euler", "tokens", "quant"};
   return (cls >= 0 && cls < H3_K_COUNT) ? names[cls] : "";
 }
 

@@ -31,10 +31,16 @@ struct GemmEpi {
   const float* gate;    // gate of segment s, column n at gate[s * gate_seg_stride + n]
   int gate_seg_stride;
   int n_text, n_prefix; // row segment boundaries
+  const float* a_scale; // int8 products: [M] row scales of A
+  const float* b_scale; // int8 products: [N] row scales of B (output columns)
 };
 bool gemm_shape_ok(int M, int N, int K);
+bool gemm_i8_shape_ok(int M, int N, int K);
 hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, int K,
                        const GemmEpi& ep, hipStream_t s);
+// int8 operands (codes), exact int32 sums scaled by a_scale[row] * b_scale[col]
+hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* B, int M, int N, int K,
+                          const GemmEpi& ep, hipStream_t s);
 
 // ---- head layout: q/k RMS norm + RoPE, padded head-major q, k, v^T, tile means
 struct HeadsArgs {
@@ -121,6 +127,16 @@ struct TimeGemvArgs {
 };
 hipError_t launch_time_gemv(const TimeGemvArgs& a, hipStream_t s);
 hipError_t launch_euler(float* x, const float* v, size_t n, double dsigma, hipStream_t s);
+
+// ---- int8 quantization ------------------------------------------------------------
+// modnorm (as launch_modnorm over rows [0, rows)) followed by the row's int8 codes
+hipError_t launch_modnorm_q(const bf16_t* x, const float* shift, const float* scale,
+                            int seg_stride, int rows, int H, int n_text, int n_prefix, float eps,
+                            int8_t* q, float* qscale, bf16_t* n_out, hipStream_t s);
+bool quant_shape_ok(int K, int G);
+// codes of x [rows][K] per group of G columns (G = K: per row); qscale [rows][K/G]
+hipError_t launch_quant_rows(const bf16_t* x, int rows, int K, int G, int8_t* q, float* qscale,
+                             hipStream_t s);
 
 // ---- token reduction ------------------------------------------------------------
 struct TokenArgs {

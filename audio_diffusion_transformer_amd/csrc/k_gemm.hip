@@ -53,6 +53,9 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int STAGE = BM * BK;  // bf16 elements of one operand in one stage (32 KB)
+constexpr int STAGE_BYTES = 128;  // bytes of K per stage and row: 64 bf16 or 128 int8
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediate that waits for vmcnt <= n and leaves expcnt and lgkmcnt
 // unchecked (gfx9 encoding: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
@@ -113,9 +116,12 @@ __device__ __forceinline__ int seg_of(int row, int n_text, int n_prefix) {
   return row < n_text ? 0 : (row < n_prefix ? 1 : 2);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__ A,
-                                                      const bf16_t* __restrict__ B, int M,
+// I8: int8 operands (v_mfma_i32_16x16x64_i8, 64 k-values per product, 128
+// per stage) with exact int32 sums, scaled in the epilogue by the row scale
+// of A and the column scale of B: acc_f = (float)acc * a_scale[row] * b_scale[col].
+template <int EPI, bool I8>
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A,
+                                                      const void* __restrict__ B, int M,
                                                       int N, int K, GemmEpi ep) {
   // two stages of (A, B); reused whole (128 KB) by the epilogue
   __shared__ __attribute__((aligned(16))) bf16_t smem[4 * STAGE];
@@ -137,18 +143,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
 
   // Loads: a stage is 256 rows x 8 chunks per operand; thread t moves chunks
   // 512 i + t (i < 4) of A and of B.  Byte offsets from the stage's column.
+  constexpr int ES = I8 ? 1 : 2;  // bytes per element
+  const int rowb = K * ES;         // bytes per operand row
   uint32_t ga[4], gb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = i * 512 + tid;
     const int r = q >> 3, gc = (q & 7) ^ swz(r);
-    ga[i] = 2u * (uint32_t)(min(m0 + r, M - 1) * K + gc * 8);  // ragged M: clamp; rows >= M are dropped
-    gb[i] = 2u * (uint32_t)((n0 + r) * K + gc * 8);
+    // byte offsets below 2^32 (M K and N K are below 2^31); ragged M: clamp, rows >= M are dropped
+    ga[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)rowb + (uint32_t)(gc * 16);
+    gb[i] = (uint32_t)(n0 + r) * (uint32_t)rowb + (uint32_t)(gc * 16);
   }
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 64 * 16);
   auto issue = [&](int s) {
-    const void* pa = uniform_ptr(A + s * BK);
-    const void* pb = uniform_ptr(B + s * BK);
+    const void* pa = uniform_ptr(static_cast<const char*>(A) + s * STAGE_BYTES);
+    const void* pb = uniform_ptr(static_cast<const char*>(B) + s * STAGE_BYTES);
     const uint32_t l = lds0 + (uint32_t)((s & 1) * 2 * STAGE * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -161,17 +170,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
   // the 8 k-values 8 (l/16) .. +7 of a 32-wide k-step (A and B alike); the
   // result block holds, in lane l, column l%16 and rows 4 (l/16) .. +3.
   const int l16 = lane & 15, q4 = lane >> 4;
-  f32x4_t acc[8][4];
+  f32x4_t acc[8][4];   // bf16 products (and the scaled int8 sums in the epilogue)
+  i32x4_t acci[8][4];  // int8 products: exact int32 sums
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        acc[i][j][e] = 0.f;
+        acci[i][j][e] = 0;
+      }
 
   // fragments of a stage (k-steps kk = 0, 1 of 32): A rows wm*128 + 16i + l%16,
   // B rows wn*64 + 16j + l%16, k-chunk 4 kk + l/16 (8 values each)
-  bf16x8_t fa[2][8], fb[2][4];
+  u32x4_t fa[2][8], fb[2][4];
   auto read_frags = [&](int s) {
     const bf16_t* sa = smem + (s & 1) * 2 * STAGE;
     const bf16_t* sb = sa + STAGE;
@@ -181,12 +194,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = wm * 128 + i * 16 + l16;
-        fa[kk][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + r * BK + (gc ^ swz(r)) * 8));
+        fa[kk][i] = *reinterpret_cast<const u32x4_t*>(sa + r * BK + (gc ^ swz(r)) * 8);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = wn * 64 + j * 16 + l16;
-        fb[kk][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + r * BK + (gc ^ swz(r)) * 8));
+        fb[kk][j] = *reinterpret_cast<const u32x4_t*>(sb + r * BK + (gc ^ swz(r)) * 8);
       }
     }
   };
@@ -196,11 +209,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (I8)
+            acci[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                __builtin_bit_cast(i32x4_t, fa[kk][i]), __builtin_bit_cast(i32x4_t, fb[kk][j]),
+                acci[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(fa[kk][i]), as_bf16x8(fb[kk][j]), acc[i][j], 0, 0, 0);
+        }
   };
 
-  const int KT = K / BK;  // >= 2
+  const int KT = rowb / STAGE_BYTES;  // >= 2
   issue(0);
   if (grp == 1) {
     issue(1);
@@ -237,6 +257,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const bf16_t* __restrict__
   // Accumulator element e of block (i, j) in lane l sits at row 4(l/16) + e,
   // column l%16 of that 16x16 block.  Each wave rounds its 128x64 sub-tile into
   // its own 16 KB of LDS, then writes it back in 16-byte chunks.
+  if constexpr (I8) {  // int32 sums -> fp32 with the row and column scales
+    float sa[8][4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sa[i][e] = ep.a_scale[min(m0 + wm * 128 + i * 16 + 4 * q4 + e, M - 1)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sb[j] = ep.b_scale[n0 + wn * 64 + j * 16 + l16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[i][j][e] = (float)acci[i][j][e] * sa[i][e] * sb[j];
+  }
   bf16_t* st = smem + wave * (128 * 64);
   if constexpr (EPI == EPI_BIAS_SWIGLU) {
     // GEMM columns 32b .. 32b+15 are the gate values of features 16b .. 16b+15
@@ -320,24 +357,41 @@ bool gemm_shape_ok(int M, int N, int K) {
          (long long)M * K < (1ll << 31) && (long long)N * K < (1ll << 31);
 }
 
+bool gemm_i8_shape_ok(int M, int N, int K) {
+  return M >= 1 && N >= BN && N % BN == 0 && K >= 4 * BK && K % (4 * BK) == 0 &&
+         (long long)M * K < (1ll << 31) && (long long)N * K < (1ll << 31);
+}
+
+template <bool I8>
+static void launch_epi(int epi, dim3 grid, dim3 block, const void* A, const void* B, int M, int N,
+                       int K, const GemmEpi& ep, hipStream_t s) {
+  switch (epi) {
+    case EPI_BIAS:
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS, I8>), grid, block, 0, s, A, B, M, N, K, ep);
+      break;
+    case EPI_BIAS_GELU:
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_GELU, I8>), grid, block, 0, s, A, B, M, N, K, ep);
+      break;
+    case EPI_BIAS_SWIGLU:
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_SWIGLU, I8>), grid, block, 0, s, A, B, M, N, K, ep);
+      break;
+    default:
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_RESGATE, I8>), grid, block, 0, s, A, B, M, N, K, ep);
+      break;
+  }
+}
+
 hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, int K,
                        const GemmEpi& ep, hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  dim3 grid(tiles), block(512);
-  switch (epi) {
-    case EPI_BIAS:
-      hipLaunchKernelGGL(k_gemm_bf16<EPI_BIAS>, grid, block, 0, s, A, B, M, N, K, ep);
-      break;
-    case EPI_BIAS_GELU:
-      hipLaunchKernelGGL(k_gemm_bf16<EPI_BIAS_GELU>, grid, block, 0, s, A, B, M, N, K, ep);
-      break;
-    case EPI_BIAS_SWIGLU:
-      hipLaunchKernelGGL(k_gemm_bf16<EPI_BIAS_SWIGLU>, grid, block, 0, s, A, B, M, N, K, ep);
-      break;
-    default:
-      hipLaunchKernelGGL(k_gemm_bf16<EPI_BIAS_RESGATE>, grid, block, 0, s, A, B, M, N, K, ep);
-      break;
-  }
+  launch_epi<false>(epi, dim3(tiles), dim3(512), A, B, M, N, K, ep, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* B, int M, int N, int K,
+                          const GemmEpi& ep, hipStream_t s) {
+  const int tiles = ((M + BM - 1) / BM) * (N / BN);
+  launch_epi<true>(epi, dim3(tiles), dim3(512), A, B, M, N, K, ep, s);
   return hipGetLastError();
 }
 

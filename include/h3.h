@@ -59,7 +59,7 @@ enum {
                            more than 512 selected tiles, padded rows above 131072 */
 };
 
-enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2 };
+enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2, H3_WS_DIT_I8 = 3 };
 
 #define H3_ABI_VERSION 3
 
@@ -133,6 +133,7 @@ typedef struct {
 typedef struct {
   size_t tables, norm, big, q, k, vt, qbar, kbar, vbar, scores, sel, pooled, attn, x1;
   size_t xa, xb;         /* residual ping-pong of h3_dit_forward (0 if unused) */
+  size_t q8, qscale;     /* int8 forward: activation codes [R][max(H, A, F)], row scales [R] */
   size_t total;
   int32_t padded_rows;   /* Rp */
   int32_t n_query_tiles; /* nQ = n_tiles - n_prefix_tiles */
@@ -278,6 +279,44 @@ int h3_dit_forward_tr(const h3_shape* shape, int32_t n_blocks, const int32_t* ti
                       const float* rope, const h3_bf16* x_in, float* vel_video,
                       float* vel_audio, void* ws, size_t ws_bytes, void* stream);
 
+/* int8 variant (h3.c README, implementation notes: the int8 QKV,
+ * attention-output and MLP products; dynamic activation quantization,
+ * per-output-channel weight scales, the quantization folded into the gated
+ * AdaLN).  Codes are symmetric: per row (or group of columns) with
+ * m = max |x|: code = clamp(rint(x * (127/m)), -127, 127), scale = m / 127,
+ * fp32 arithmetic with IEEE division; zero rows have codes 0 and scale 0. */
+
+/* Codes of a bf16 matrix x [rows][cols] per row (group = 0) or per group of
+ * `group` consecutive columns: q int8 [rows][cols], scale fp32
+ * [rows][cols / group] (or [rows]).  Device pointers; cols and group multiples
+ * of 8, group <= 32768 and dividing cols.  Weights are quantized once with this
+ * call (per output channel: group = 0). */
+int h3_quantize_rows(const h3_bf16* x, int32_t rows, int32_t cols, int32_t group, int8_t* q,
+                     float* scale, void* stream);
+
+/* One block's int8 weights: codes and per-output-row scales of the four
+ * products (h3_quantize_rows with group 0), the other tensors as in
+ * h3_block_weights. */
+typedef struct {
+  const int8_t* w_qkv; const float* s_qkv; const h3_bf16* b_qkv;
+  const h3_bf16 *q_gain, *k_gain;
+  const int8_t* w_o;   const float* s_o;   const h3_bf16* b_o;
+  const int8_t* w_fc1; const float* s_fc1; const h3_bf16* b_fc1;
+  const int8_t* w_fc2; const float* s_fc2; const h3_bf16* b_fc2;
+} h3_block_weights_i8;
+
+/* h3_dit_forward with int8 products: each block's QKV, out-projection, FC1
+ * and FC2 inputs are quantized per row (the norm outputs inside the fused
+ * norm kernel), the products are exact int32 sums scaled by the row and
+ * column scales, all else as in h3_dit_forward (attention in bf16).
+ * The hidden, attention and FFN widths (K of the products) must be multiples
+ * of 256.  Workspace: H3_WS_DIT_I8. */
+int h3_dit_forward_i8(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_start,
+                      const h3_block_weights_i8* blocks, const h3_head_weights* heads,
+                      const float* mod, const float* mod_final, const float* rope,
+                      const h3_bf16* x_in, float* vel_video, float* vel_audio, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* Kernel-time accounting for diagnostics: while enabled, each kernel launch
  * of the library is bracketed by HIP events on its stream.  h3_prof_read
  * synchronizes those events and returns, for kernel class `cls` (H3_K_*),
@@ -285,7 +324,7 @@ int h3_dit_forward_tr(const h3_shape* shape, int32_t n_blocks, const int32_t* ti
  * the events it has read.  Not thread-safe; for benchmarks. */
 enum { H3_K_NORM = 0, H3_K_GEMM_QKV, H3_K_HEADS, H3_K_ROUTE, H3_K_ATTN, H3_K_GEMM_O,
        H3_K_GEMM_FC1, H3_K_GEMM_FC2, H3_K_FINAL, H3_K_TABLES, H3_K_ROWS_IN, H3_K_TIME,
-       H3_K_EULER, H3_K_TOKENS, H3_K_COUNT };
+       H3_K_EULER, H3_K_TOKENS, H3_K_QUANT, H3_K_COUNT };
 int h3_prof_enable(int on);
 int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms);
 const char* h3_prof_kernel_name(int32_t cls);

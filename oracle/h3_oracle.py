@@ -670,17 +670,18 @@ def linear_int8(qa, sa, qw, sw, b, group=0):
     """y = sum_k qa qw * sa * sw + b: exact integer sums, then the scales in
     float64.  With `group`, sa is [n][K/group] and each group's sum takes its
     own activation scale."""
-    qa64, qw64 = qa.astype(np.int64), qw.astype(np.int64)
+    # integer sums in float64 matrix products: every partial sum is an
+    # integer below 127^2 K < 2^53, so they are exact
+    qa64, qw64 = qa.astype(np.float64), qw.astype(np.float64)
     swf = np.asarray(sw, dtype=np.float64)
     if group == 0:
-        acc = (qa64 @ qw64.T).astype(np.float64)
+        acc = qa64 @ qw64.T
         return acc * np.asarray(sa, dtype=np.float64)[:, None] * swf[None, :] + b
     n, K = qa.shape
     y = np.zeros((n, qw.shape[0]))
     for gi in range(K // group):
         sl = slice(gi * group, (gi + 1) * group)
-        y += (qa64[:, sl] @ qw64[:, sl].T).astype(np.float64) * \
-            np.asarray(sa, dtype=np.float64)[:, gi:gi + 1]
+        y += (qa64[:, sl] @ qw64[:, sl].T) * np.asarray(sa, dtype=np.float64)[:, gi:gi + 1]
     return y * swf[None, :] + b
 
 
