@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_I8_TOPS = 5000.0       # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 N_BLOCKS = 50
 N_PASSES = 8                # denoising passes of --denoise (the pages' 8-step schedule)
@@ -54,6 +55,9 @@ def parse():
     ap.add_argument("--token-reduction", action="store_true",
                     help="with --workload fasth3: blocks 4 .. 39 on the pooled stream (pairs of "
                          "horizontally adjacent video tokens), as in the pages' early passes")
+    ap.add_argument("--int8", action="store_true",
+                    help="the forward with int8 products (h3_dit_forward_i8): weights quantized "
+                         "per output row, activations per row; attention stays bf16")
     ap.add_argument("--denoise", action="store_true",
                     help="time h3_denoise instead: 8 passes of rows in, modulation tables, "
                          "the 50-block forward and heads, and the Euler step, per timed step")
@@ -357,8 +361,15 @@ def main():
     torch.cuda.set_device(0)
     print(f"setup: {L} blocks of weights on {torch.cuda.get_device_name(0)}", file=sys.stderr,
           flush=True)
-    blocks = [S.device_block_weights(sh, block=l) for l in range(L)]
-    warr = (B.H3BlockWeights * L)(*[B.block_weights_struct(b) for b in blocks])
+    if args.int8:  # quantize block by block (the bf16 copies are released)
+        blocks = []
+        for l in range(L):
+            blocks.append(B.quantize_block(S.device_block_weights(sh, block=l)))
+            torch.cuda.synchronize()
+        warr = (B.H3BlockWeightsI8 * L)(*[B.block_weights_i8_struct(b) for b in blocks])
+    else:
+        blocks = [S.device_block_weights(sh, block=l) for l in range(L)]
+        warr = (B.H3BlockWeights * L)(*[B.block_weights_struct(b) for b in blocks])
     heads = {k: T.to_dev(v) for k, v in S.head_weights(sh).items()}
     hw = B.head_weights_struct(heads)
     n_fwd = args.warmup + args.steps
@@ -369,12 +380,14 @@ def main():
     x = T.to_dev(S.activations(sh, field=True))
     vv = torch.empty((sh.n_video, sh.c_video), dtype=torch.float32, device=dev)
     va = torch.empty((sh.n_audio, sh.c_audio), dtype=torch.float32, device=dev)
-    ws = T.workspace(B.workspace_bytes(shape, ts, B.H3_WS_DIT))
+    ws = T.workspace(B.workspace_bytes(shape, ts, B.H3_WS_DIT_I8 if args.int8 else B.H3_WS_DIT))
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     print("setup done", file=sys.stderr, flush=True)
 
     tr = None
+    if args.token_reduction and args.int8:
+        raise SystemExit("--token-reduction and --int8 are separate variants")
     if args.token_reduction:
         if not sh.cube:
             raise SystemExit("--token-reduction needs a video grid: use --workload fasth3")
@@ -386,7 +399,10 @@ def main():
         ws = T.workspace(B.dit_forward_tr_workspace_bytes(shape, ts, tr))
 
     def forward(s):
-        if tr is None:
+        if args.int8:
+            B.dit_forward_i8(shape, ts, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws,
+                             stream=stream)
+        elif tr is None:
             B.dit_forward(shape, ts, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws,
                           stream=stream)
         else:
@@ -432,7 +448,8 @@ def main():
             kind, amount = work[name]
             if kind == "mfma":
                 ach = amount / (avg * 1e-3) / 1e12
-                entry.update(achieved_tflops=round(ach, 1), frac=round(ach / PEAK_BF16_TFLOPS, 4))
+                peak = PEAK_I8_TOPS if args.int8 and name.startswith("gemm_") else PEAK_BF16_TFLOPS
+                entry.update(achieved_tflops=round(ach, 1), frac=round(ach / peak, 4))
             else:
                 ach = amount / (avg * 1e-3) / 1e9
                 entry.update(achieved_gbs=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 4))
@@ -443,9 +460,11 @@ def main():
         kind, amount = work[dom]
         e = kernels[dom]
         if kind == "mfma":
+            i8 = args.int8 and dom.startswith("gemm_")
             roofline = {"bound": "mfma", "kernel": dom, "achieved": e["achieved_tflops"],
-                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": e["frac"],
-                        "traffic": measured_traffic(dom)}
+                        "peak": PEAK_I8_TOPS if i8 else PEAK_BF16_TFLOPS,
+                        "unit": "TOP/s (int8)" if i8 else "TFLOP/s", "frac": e["frac"],
+                        "traffic": None if args.int8 else measured_traffic(dom)}
         else:
             roofline = {"bound": "hbm", "kernel": dom, "achieved": e["achieved_gbs"],
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": e["frac"],
@@ -453,14 +472,16 @@ def main():
         gemm_flop = sum(work[k][1] * kernels[k]["launches"] for k in kernels
                         if k.startswith("gemm_"))
         gemm_ms = sum(kernels[k]["total_ms"] for k in kernels if k.startswith("gemm_"))
-        roofline["gemm_all_frac"] = round(gemm_flop / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        roofline["gemm_all_frac"] = round(gemm_flop / (gemm_ms * 1e-3) / 1e12 /
+                                          (PEAK_I8_TOPS if args.int8 else PEAK_BF16_TFLOPS), 4)
 
     srt = sorted(step_ms)
     line = {
         "metric": ("s per 50-block DiT forward at 15,435 rows; GEMM/attn % of bf16 MFMA peak"
                    if args.workload == "full" else
                    "s per 50-block FastH3 forward at 15,435 rows (the pages' block and geometry)"
-                   + (", token reduction in blocks 4-39" if tr is not None else "")),
+                   + (", token reduction in blocks 4-39" if tr is not None else ""))
+                  + (", int8 products" if args.int8 else ""),
         "value": round(ms_per_step / 1e3, 5),
         "unit": "s",
         "n_gpus": 1,
@@ -472,8 +493,8 @@ def main():
         # the pages time this same forward (FastH3 geometry, 50 blocks) at 10.1 s
         # on an Apple M5 Ultra: another machine, a ratio for context only
         "vs_baseline": (round(ms_per_step / 1e3 / PAGES_FASTH3_S, 4)
-                        if args.workload == "fasth3" and tr is None else None),
-        "dtype": "bf16",
+                        if args.workload == "fasth3" and tr is None and not args.int8 else None),
+        "dtype": "int8 products, bf16 attention" if args.int8 else "bf16",
         "data": "synthetic",
         "config": {"workload": (f"{L}-block H3-style DiT forward, 15,435 rows (512 text / 543 "
                                 f"audio / 14,380 video), hidden 5120, 40x128 heads, GELU FFN "
