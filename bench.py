@@ -81,10 +81,10 @@ TRAFFIC = {
     "sources": ["audio_diffusion_transformer_amd/csrc/k_gemm.hip",
                 "audio_diffusion_transformer_amd/csrc/common.h",
                 "audio_diffusion_transformer_amd/csrc/internal.h"],
-    "sources_sha256": "ec45c21f772d6ad65560689a29595d2eb5798fe67a80a98cea1404411b5e12e9",
+    "sources_sha256": "fd0aa481863f2bffaab0385c7548c8321e9fea738206677037f07d563faec5f6",
     # raw KiB per dispatch and the copy's scale factors (1 GiB copy: FETCH_SIZE
     # 524294.5 KiB, WRITE_SIZE 1048576.0 KiB)
-    "fetch_kib": 2583991.75, "fetch_scale": 1.999975,
+    "fetch_kib": 2545105.0625, "fetch_scale": 1.999975,
     "write_kib": 617400.0, "write_scale": 1.000000,
 }
 
