@@ -182,7 +182,9 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
     size_t w8 = H > A ? H : A;
     if ((size_t)p.F > w8) w8 = p.F;
     L.q8 = take(R * w8);
-    L.qscale = take(R * f4);
+    // row scales, or one per row and 1,024 channels of the FC2 input
+    const size_t ng = p.F % kFc2Group == 0 ? (size_t)(p.F / kFc2Group) : 1;
+    L.qscale = take(R * (ng > 1 ? ng : 1) * f4);
   }
   L.total = off;
   L.padded_rows = p.Rp;
@@ -471,8 +473,11 @@ int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const fl
                         R, p.F1, H, e, st));
   prof_end(H3_K_GEMM_FC1, st);
 
+  // the FC2 input: one scale per 1,024 channels (per row when F is not a
+  // multiple of 1,024)
+  const bool grouped = F % kFc2Group == 0 && F > kFc2Group;
   prof_begin(H3_K_QUANT, st);
-  H3_TRY(launch_quant_rows(big, R, F, F, q8, qs, st));
+  H3_TRY(launch_quant_rows(big, R, F, grouped ? kFc2Group : F, q8, qs, st));
   prof_end(H3_K_QUANT, st);
   e = GemmEpi{};
   e.bias = w->b_fc2;
@@ -485,7 +490,10 @@ int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const fl
   e.a_scale = qs;
   e.b_scale = w->s_fc2;
   prof_begin(H3_K_GEMM_FC2, st);
-  H3_TRY(launch_gemm_i8(EPI_BIAS_RESGATE, q8, w->w_fc2, R, H, F, e, st));
+  if (grouped)
+    H3_TRY(launch_gemm_i8g_resgate(q8, w->w_fc2, R, H, F, kFc2Group, e, st));
+  else
+    H3_TRY(launch_gemm_i8(EPI_BIAS_RESGATE, q8, w->w_fc2, R, H, F, e, st));
   prof_end(H3_K_GEMM_FC2, st);
   return H3_OK;
 }

@@ -41,6 +41,12 @@ hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, 
 // int8 operands (codes), exact int32 sums scaled by a_scale[row] * b_scale[col]
 hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* B, int M, int N, int K,
                           const GemmEpi& ep, hipStream_t s);
+// int8 product with one A scale per row and group of G = kFc2Group k-values
+// (a_scale [M][K/G]), gated-residual epilogue
+constexpr int kFc2Group = 1024;
+bool gemm_i8g_shape_ok(int M, int N, int K, int G);
+hipError_t launch_gemm_i8g_resgate(const int8_t* A, const int8_t* B, int M, int N, int K, int G,
+                                   const GemmEpi& ep, hipStream_t s);
 
 // ---- head layout: q/k RMS norm + RoPE, padded head-major q, k, v^T, tile means
 struct HeadsArgs {

@@ -350,6 +350,193 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
   }
 }
 
+// int8 product whose A rows carry one scale per group of G consecutive k
+// (the FC2 input: one scale per 1,024 channels), with the gated-residual
+// epilogue.  The int32 sums of each group are scaled by their row's group
+// scale and added to fp32 sums, so every lane holds two sets of accumulators;
+// to keep them within the registers of two waves per SIMD the workgroup tile
+// is 128 x 256 (wave tile 64 x 64 as 4 x 4 blocks).  Loads, LDS layout and the
+// ping-pong schedule are those of k_gemm_bf16 (A half the rows: 6 loads per
+// wave and stage instead of 8).
+constexpr int BMG = 128;
+
+template <int G>
+__global__ __launch_bounds__(512, 1) void k_gemm_i8g(const int8_t* __restrict__ A,
+                                                     const int8_t* __restrict__ B, int M, int N,
+                                                     int K, GemmEpi ep) {
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BMG + BN) * 64];  // 2 x 48 KB
+  constexpr int SA = BMG * 64, SB = BN * 64, SST = SA + SB;  // bf16-element sizes (128 B rows)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles_m = (M + BMG - 1) / BMG, tiles_n = N / BN;
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int q8 = nb >> 3, r8 = nb & 7, xcd = bid & 7, idx = bid >> 3;
+  const int lin = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int gq = lin / per_group;
+  const int first_m = gq * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (lin % per_group) % gsize;
+  const int tn = (lin % per_group) / gsize;
+  const int m0 = tm * BMG, n0 = tn * BN;
+  const int grp = wave >> 2, wm = wave >> 2, wn = wave & 3;
+
+  const uint32_t rowb = (uint32_t)K;
+  uint32_t ga[2], gb[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = i * 512 + tid;
+    const int r = q >> 3, gc = (q & 7) ^ swz(r);
+    ga[i] = (uint32_t)min(m0 + r, M - 1) * rowb + (uint32_t)(gc * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = i * 512 + tid;
+    const int r = q >> 3, gc = (q & 7) ^ swz(r);
+    gb[i] = (uint32_t)(n0 + r) * rowb + (uint32_t)(gc * 16);
+  }
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 64 * 16);
+  auto issue = [&](int s) {
+    const void* pa = uniform_ptr(A + s * STAGE_BYTES);
+    const void* pb = uniform_ptr(B + s * STAGE_BYTES);
+    const uint32_t l = lds0 + (uint32_t)((s & 1) * SST * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(pa, ga[i], l + i * 512 * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(pb, gb[i], l + SA * 2 + i * 512 * 16);
+  };
+
+  const int l16 = lane & 15, q4 = lane >> 4;
+  i32x4_t acci[4][4];
+  f32x4_t accf[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acci[i][j][e] = 0;
+        accf[i][j][e] = 0.f;
+      }
+  u32x4_t fa[2][4], fb[2][4];
+  auto read_frags = [&](int s) {
+    const bf16_t* sa = smem + (s & 1) * SST;
+    const bf16_t* sb = sa + SA;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int gc = kk * 4 + q4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + l16;
+        fa[kk][i] = *reinterpret_cast<const u32x4_t*>(sa + r * BK + (gc ^ swz(r)) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 64 + j * 16 + l16;
+        fb[kk][j] = *reinterpret_cast<const u32x4_t*>(sb + r * BK + (gc ^ swz(r)) * 8);
+      }
+    }
+  };
+  auto products = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acci[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              __builtin_bit_cast(i32x4_t, fa[kk][i]), __builtin_bit_cast(i32x4_t, fb[kk][j]),
+              acci[i][j], 0, 0, 0);
+  };
+  const int ng = K / G;  // groups per row
+  // the end of a group: fp32 sums += int32 sums * the rows' group scales
+  auto flush = [&](int gi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = min(m0 + wm * 64 + i * 16 + 4 * q4 + e, M - 1);
+        const float sc = ep.a_scale[(size_t)row * ng + gi];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          accf[i][j][e] = fmaf((float)acci[i][j][e], sc, accf[i][j][e]);
+          acci[i][j][e] = 0;
+        }
+      }
+  };
+
+  const int KT = K / STAGE_BYTES;  // >= 2
+  constexpr int SPG = G / STAGE_BYTES;  // stages per group
+  issue(0);
+  if (grp == 1) {
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(H3_VMCNT(6));
+  } else {
+    __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+  }
+  phase_barrier();
+  if (grp == 1) phase_barrier();
+  for (int s = 0; s < KT; ++s) {
+    if (grp == 0 && s + 1 < KT) issue(s + 1);
+    read_frags(s);
+    __builtin_amdgcn_s_waitcnt(H3_LGKMCNT0);
+    if (grp == 1) {
+      if (s + 2 < KT) {
+        issue(s + 2);
+        __builtin_amdgcn_s_waitcnt(H3_VMCNT(6));
+      } else {
+        __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+      }
+    }
+    phase_barrier();
+    products();
+    if ((s + 1) % SPG == 0) flush(s / SPG);
+    if (grp == 0 && s + 1 < KT) __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- epilogue: bias, bf16, gated residual (as EPI_BIAS_RESGATE) ----
+  bf16_t* st = smem + wave * (64 * 64);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = n0 + wn * 64 + j * 16 + l16;
+    const float sbv = ep.b_scale[col], bias = bf2f(ep.bias[col]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = i * 16 + 4 * q4 + e;
+        st[r * 64 + j * 16 + l16] = f2bf(accf[i][j][e] * sbv + bias);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+  for (int t = 0; t < 8; ++t) {
+    const int q = t * 64 + lane;
+    const int r = q >> 3, c8 = (q & 7) * 8;
+    const int row = m0 + wm * 64 + r;
+    if (row >= M) continue;
+    const int col = n0 + wn * 64 + c8;
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + r * 64 + c8);
+    const size_t o = (size_t)row * N + col;
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ep.res + o);
+    const float* gp =
+        ep.gate + (size_t)seg_of(row, ep.n_text, ep.n_prefix) * ep.gate_seg_stride + col;
+    const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
+    const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gp + 4);
+    const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2)
+      v[t2] = pack2(fmaf(gv[2 * t2], bflo(v[t2]), bflo(x[t2])),
+                    fmaf(gv[2 * t2 + 1], bfhi(v[t2]), bfhi(x[t2])));
+    *reinterpret_cast<u32x4_t*>(ep.out + o) = v;
+  }
+}
+
 }  // namespace
 
 bool gemm_shape_ok(int M, int N, int K) {
@@ -385,6 +572,18 @@ hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, 
                        const GemmEpi& ep, hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   launch_epi<false>(epi, dim3(tiles), dim3(512), A, B, M, N, K, ep, s);
+  return hipGetLastError();
+}
+
+bool gemm_i8g_shape_ok(int M, int N, int K, int G) {
+  return G == kFc2Group && K % G == 0 && gemm_i8_shape_ok(M, N, K);
+}
+
+hipError_t launch_gemm_i8g_resgate(const int8_t* A, const int8_t* B, int M, int N, int K, int G,
+                                   const GemmEpi& ep, hipStream_t s) {
+  if (G != kFc2Group) return hipErrorInvalidValue;
+  const int tiles = ((M + BMG - 1) / BMG) * (N / BN);
+  hipLaunchKernelGGL((k_gemm_i8g<kFc2Group>), dim3(tiles), dim3(512), 0, s, A, B, M, N, K, ep);
   return hipGetLastError();
 }
 

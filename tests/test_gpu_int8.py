@@ -64,16 +64,24 @@ def _run_i8(sh, ts, npt, blocks, mods, head, mf, rope, x):
     return vv.cpu().numpy(), va.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["tiny", "fasth3_tiny"])
+def fc2_group(sh):
+    """The FC2 input is quantized per 1,024 channels when the FFN width is a
+    larger multiple of 1,024, else per row."""
+    return 1024 if sh.ffn % 1024 == 0 and sh.ffn > 1024 else 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_grouped_fc2", "fasth3_tiny"])
 def test_int8_forward(name):
     # (the int8 products need K multiples of 256: the pages' block with 8 heads of 64)
-    sh = S.TINY if name == "tiny" else S.FASTH3_TINY.replace(n_heads=8)
+    sh = {"tiny": S.TINY, "tiny_grouped_fc2": S.TINY.replace(ffn=3072),
+          "fasth3_tiny": S.FASTH3_TINY.replace(n_heads=8)}[name]
     L = 2
     print(f"case: int8 forward {name} L={L}", flush=True)
     ts, npt, blocks, mods, head, mf, rope, x = _i8_case(sh, L)
     gv, ga = _run_i8(sh, ts, npt, blocks, mods, head, mf, rope, x)
     qws = [O.quantize_block_int8(b) for b in blocks]
-    r = O.dit_forward(sh, ts, npt, blocks, head, mods, mf, rope, x, qws=qws)
+    r = O.dit_forward(sh, ts, npt, blocks, head, mods, mf, rope, x, qws=qws,
+                      fc2_group=fc2_group(sh))
     for got, ref in ((gv, r["vel_video"]), (ga, r["vel_audio"])):
         m = P.metrics(got, ref)
         assert m["cos"] >= 0.9999 and m["rel"] <= 5e-3, m
@@ -83,3 +91,45 @@ def test_int8_forward(name):
     m = P.metrics(gv, rb["vel_video"])
     print("int8 vs bf16 video velocity:", m, flush=True)
     assert m["cos"] >= 0.99, m
+
+
+def test_int8_full_size_block_sampled_rows():
+    """Hidden 5120, 40 x 128 heads, GELU FFN 20480 (the FC2 input in 20 groups
+    of 1,024), 15,435 rows; one int8 block through h3_dit_forward_i8 (its
+    output stays in the workspace), the oracle on sampled rows."""
+    sh = S.FULL
+    print("case: int8 full-size block (oracle on sampled rows)", flush=True)
+    ts, npt = S.tile_map(sh)
+    w = S.block_weights(sh)
+    mod = S.modulation(sh)
+    rope = S.rope_tables(sh)
+    x = S.activations(sh, field=True)
+    shape = B.make_shape(sh, ts, npt)
+    lay = B.workspace_layout(shape, ts, B.H3_WS_DIT_I8)
+    ws = T.workspace(lay.total)
+    qb = B.quantize_block(T.weights_to_dev(w))
+    vv = torch.empty((sh.n_video, sh.c_video), dtype=torch.float32, device="cuda")
+    va = torch.empty((sh.n_audio, sh.c_audio), dtype=torch.float32, device="cuda")
+    B.dit_forward_i8(shape, ts, [qb], T.weights_to_dev(S.head_weights(sh)),
+                     T.to_dev(mod[None]), T.to_dev(S.final_modulation(sh)), T.to_dev(rope),
+                     T.to_dev(x), vv, va, ws)
+    torch.cuda.synchronize()
+    R, H, A = sh.rows, sh.hidden, sh.attn_width
+    wsh = ws.cpu().numpy()
+
+    def view(off, shp):
+        n = int(np.prod(shp)) * 2
+        return T.bf16_bits_to_f64(wsh[off:off + n].view(np.uint16).reshape(shp))
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(510, 516), np.arange(1050, 1060),
+                                     np.arange(8000, 8040), np.arange(R - 30, R)]))
+    print("oracle ...", flush=True)
+    r = O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows,
+                        qw=O.quantize_block_int8(w), fc2_group=fc2_group(sh))
+    m = P.metrics(view(lay.attn, (R, A))[rows], r["attn"])
+    assert m["cos"] > 0.9999 and m["rel"] < 1e-2, ("attn", m)
+    for name, off in (("x1", lay.x1), ("x2", lay.xa)):
+        got = view(off, (R, H))[rows]
+        d = P.metrics(got - T.bf16_bits_to_f64(x)[rows], r[name] - T.bf16_bits_to_f64(x)[rows])
+        # the block's update of the residual (a one-step code flip moves a
+        # product by about one code step, 1/127 of its row's range)
+        assert d["cos"] > 0.999 and d["rel"] < 2e-2, (name, d)
