@@ -132,7 +132,7 @@ def lib():
     L.h3_dit_forward_i8.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32, i32p,
                                     ctypes.POINTER(H3BlockWeightsI8),
                                     ctypes.POINTER(H3HeadWeights), _vp, _vp, _vp, _vp, _vp, _vp,
-                                    _vp, ctypes.c_size_t, _vp]
+                                    ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
     L.h3_prof_enable.argtypes = [ctypes.c_int]
     L.h3_prof_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                ctypes.POINTER(ctypes.c_double)]
@@ -361,8 +361,9 @@ def block_weights_i8_struct(w):
 
 
 def dit_forward_i8(shape, tile_start, blocks, heads, mod, mod_final, rope, x_in, vel_video,
-                   vel_audio, ws, stream=None):
-    """blocks: list of int8 weight dicts (quantize_block) or a prebuilt array."""
+                   vel_audio, ws, fc2_group=1024, stream=None):
+    """blocks: list of int8 weight dicts (quantize_block) or a prebuilt array.
+    fc2_group: 1024 (the FC2 input per 1,024 channels) or 0 (per row)."""
     ts, tp = _tiles(tile_start)
     if isinstance(blocks, (list, tuple)):
         arr = (H3BlockWeightsI8 * max(len(blocks), 1))(*[block_weights_i8_struct(b) for b in blocks])
@@ -372,8 +373,8 @@ def dit_forward_i8(shape, tile_start, blocks, heads, mod, mod_final, rope, x_in,
     hw = head_weights_struct(heads) if isinstance(heads, dict) else heads
     _check(lib().h3_dit_forward_i8(ctypes.byref(shape), n, tp, arr, ctypes.byref(hw), _ptr(mod),
                                    _ptr(mod_final), _ptr(rope), _ptr(x_in), _ptr(vel_video),
-                                   _ptr(vel_audio), _ptr(ws), ws.numel() * ws.element_size(),
-                                   _stream(stream)))
+                                   _ptr(vel_audio), int(fc2_group), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def prof_enable(on=True):

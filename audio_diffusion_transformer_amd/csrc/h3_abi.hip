@@ -402,7 +402,8 @@ int check_block_weights_i8(const h3_block_weights_i8* w, int l) {
 // The block with int8 products: the norms emit row codes, the attention output
 // and the MLP hidden are quantized per row before their products.
 int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const float* mod,
-                 const float* rope, const bf16_t* x_in, bf16_t* x_out, hipStream_t st) {
+                 const float* rope, const bf16_t* x_in, bf16_t* x_out, bool grouped,
+                 hipStream_t st) {
   const int R = p.R, H = p.H, F = p.F, A = p.A;
   const int nt = p.s.n_text, np_ = p.P;
   bf16_t* big = at<bf16_t>(ws, p.lay.big);
@@ -473,9 +474,7 @@ int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const fl
                         R, p.F1, H, e, st));
   prof_end(H3_K_GEMM_FC1, st);
 
-  // the FC2 input: one scale per 1,024 channels (per row when F is not a
-  // multiple of 1,024)
-  const bool grouped = F % kFc2Group == 0 && F > kFc2Group;
+  // the FC2 input: per row, or one scale per 1,024 channels
   prof_begin(H3_K_QUANT, st);
   H3_TRY(launch_quant_rows(big, R, F, grouped ? kFc2Group : F, q8, qs, st));
   prof_end(H3_K_QUANT, st);
@@ -986,11 +985,17 @@ int h3_quantize_rows(const h3_bf16* x, int32_t rows, int32_t cols, int32_t group
 int h3_dit_forward_i8(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_start,
                       const h3_block_weights_i8* blocks, const h3_head_weights* heads,
                       const float* mod, const float* mod_final, const float* rope,
-                      const h3_bf16* x_in, float* vel_video, float* vel_audio, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      const h3_bf16* x_in, float* vel_video, float* vel_audio,
+                      int32_t fc2_group, void* ws, size_t ws_bytes, void* stream) {
   Plan p;
   int rc = make_plan(shape, tile_start, H3_WS_DIT_I8, p);
   if (rc) return rc;
+  if (fc2_group != 0 && fc2_group != kFc2Group)
+    return fail(H3_EINVAL, "fc2_group must be 0 or %d", kFc2Group);
+  if (fc2_group && p.F % kFc2Group != 0)
+    return fail(H3_EUNSUPPORTED, "fc2_group %d needs an FFN width that is a multiple of it",
+                fc2_group);
+  const bool grouped = fc2_group != 0 && p.F > kFc2Group;  // one group = per row
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
   if (n_blocks < 0) return fail(H3_EINVAL, "n_blocks < 0");
   if (n_blocks > 0 && !blocks) return fail(H3_EINVAL, "blocks is NULL");
@@ -1011,7 +1016,8 @@ int h3_dit_forward_i8(const h3_shape* shape, int32_t n_blocks, const int32_t* ti
   for (int l = 0; l < n_blocks; ++l) {
     bf16_t* xa = at<bf16_t>(ws, p.lay.xa);
     bf16_t* xo = x == xa ? at<bf16_t>(ws, p.lay.xb) : xa;
-    if ((rc = run_block_i8(p, ws, &blocks[l], mod + l * mstride, rope, x, xo, st))) return rc;
+    if ((rc = run_block_i8(p, ws, &blocks[l], mod + l * mstride, rope, x, xo, grouped, st)))
+      return rc;
     x = xo;
   }
   return run_dit(p, ws, 0, nullptr, heads, mod, mod_final, rope, x, vel_video, vel_audio, st);

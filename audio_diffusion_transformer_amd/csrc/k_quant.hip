@@ -16,7 +16,7 @@
 //   can be written as well, for diagnostics).
 // k_quant_rows: codes of a bf16 matrix, per row or per group; one workgroup
 //   per row, each group's values held in registers between the max and the
-//   codes.
+//   codes.  k_quant_groups: groups of at most 2,048 values, one wave each.
 #include "common.h"
 #include "internal.h"
 
@@ -147,6 +147,45 @@ __global__ __launch_bounds__(256) void k_quant_rows(const bf16_t* __restrict__ x
   }
 }
 
+// one wave per (row, group) of G <= 2048 values: lanes hold G/512 16-byte vectors
+template <int NV>
+__global__ __launch_bounds__(256) void k_quant_groups(const bf16_t* __restrict__ x, int rows,
+                                                      int K, int G, int8_t* __restrict__ q,
+                                                      float* __restrict__ qscale) {
+  const int lane = threadIdx.x & 63;
+  const int ng = K / G;
+  const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= (long)rows * ng) return;
+  const int row = (int)(wid / ng), gi = (int)(wid % ng);
+  const size_t base = (size_t)row * K + (size_t)gi * G;
+  const int nu = G / 8;
+  u32x4_t v[NV];
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int u = lane + 64 * j;
+    if (u < nu) {
+      v[j] = reinterpret_cast<const u32x4_t*>(x + base)[u];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) m = fmaxf(m, fmaxf(fabsf(bflo(v[j][t])), fabsf(bfhi(v[j][t]))));
+    }
+  }
+  m = wave_max(m);
+  const float inv = m > 0.f ? 127.0f / m : 0.f;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(q + base);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int u = lane + 64 * j;
+    if (u < nu) {
+      u32x2_t w;
+      w[0] = codes4(bflo(v[j][0]), bfhi(v[j][0]), bflo(v[j][1]), bfhi(v[j][1]), inv);
+      w[1] = codes4(bflo(v[j][2]), bfhi(v[j][2]), bflo(v[j][3]), bfhi(v[j][3]), inv);
+      *reinterpret_cast<u32x2_t*>(dst + 2 * u) = w;
+    }
+  }
+  if (lane == 0) qscale[(size_t)row * ng + gi] = m / 127.0f;
+}
+
 }  // namespace
 
 hipError_t launch_modnorm_q(const bf16_t* x, const float* shift, const float* scale,
@@ -165,7 +204,15 @@ bool quant_shape_ok(int K, int G) {
 hipError_t launch_quant_rows(const bf16_t* x, int rows, int K, int G, int8_t* q, float* qscale,
                              hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quant_rows, dim3(rows), dim3(256), 0, s, x, K, G, q, qscale);
+  if (G < K && G <= 2048) {  // small groups: a wave each
+    const long waves = (long)rows * (K / G);
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (G <= 512) hipLaunchKernelGGL(k_quant_groups<1>, grid, dim3(256), 0, s, x, rows, K, G, q, qscale);
+    else if (G <= 1024) hipLaunchKernelGGL(k_quant_groups<2>, grid, dim3(256), 0, s, x, rows, K, G, q, qscale);
+    else hipLaunchKernelGGL(k_quant_groups<4>, grid, dim3(256), 0, s, x, rows, K, G, q, qscale);
+  } else {
+    hipLaunchKernelGGL(k_quant_rows, dim3(rows), dim3(256), 0, s, x, K, G, q, qscale);
+  }
   return hipGetLastError();
 }
 

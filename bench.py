@@ -57,7 +57,10 @@ def parse():
                          "horizontally adjacent video tokens), as in the pages' early passes")
     ap.add_argument("--int8", action="store_true",
                     help="the forward with int8 products (h3_dit_forward_i8): weights quantized "
-                         "per output row, activations per row; attention stays bf16")
+                         "per output row, activations per row, the FC2 input per 1,024 "
+                         "channels (the pages' default); attention stays bf16")
+    ap.add_argument("--int8-row-fc2", action="store_true",
+                    help="with --int8: the FC2 input per row (the pages' faster option)")
     ap.add_argument("--denoise", action="store_true",
                     help="time h3_denoise instead: 8 passes of rows in, modulation tables, "
                          "the 50-block forward and heads, and the Euler step, per timed step")
@@ -401,7 +404,7 @@ def main():
     def forward(s):
         if args.int8:
             B.dit_forward_i8(shape, ts, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws,
-                             stream=stream)
+                             fc2_group=0 if args.int8_row_fc2 else 1024, stream=stream)
         elif tr is None:
             B.dit_forward(shape, ts, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws,
                           stream=stream)
@@ -481,7 +484,8 @@ def main():
                    if args.workload == "full" else
                    "s per 50-block FastH3 forward at 15,435 rows (the pages' block and geometry)"
                    + (", token reduction in blocks 4-39" if tr is not None else ""))
-                  + (", int8 products" if args.int8 else ""),
+                  + ((", int8 products, FC2 input per row" if args.int8_row_fc2 else
+                      ", int8 products") if args.int8 else ""),
         "value": round(ms_per_step / 1e3, 5),
         "unit": "s",
         "n_gpus": 1,

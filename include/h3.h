@@ -305,17 +305,19 @@ typedef struct {
   const int8_t* w_fc2; const float* s_fc2; const h3_bf16* b_fc2;
 } h3_block_weights_i8;
 
-/* h3_dit_forward with int8 products: each block's QKV, out-projection, FC1
- * and FC2 inputs are quantized per row (the norm outputs inside the fused
- * norm kernel), the products are exact int32 sums scaled by the row and
- * column scales, all else as in h3_dit_forward (attention in bf16).
- * The hidden, attention and FFN widths (K of the products) must be multiples
- * of 256.  Workspace: H3_WS_DIT_I8. */
+/* h3_dit_forward with int8 products: each block's QKV, out-projection and
+ * FC1 inputs are quantized per row (the norm outputs inside the fused norm
+ * kernel), the FC2 input per row (fc2_group = 0) or per row and 1,024
+ * channels (fc2_group = 1024, the pages' default; needs an FFN width that is
+ * a multiple of 1,024); the products are exact int32 sums scaled by the row
+ * (group) and column scales, all else as in h3_dit_forward (attention in
+ * bf16).  The hidden, attention and FFN widths (K of the products) must be
+ * multiples of 256.  Workspace: H3_WS_DIT_I8. */
 int h3_dit_forward_i8(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_start,
                       const h3_block_weights_i8* blocks, const h3_head_weights* heads,
                       const float* mod, const float* mod_final, const float* rope,
-                      const h3_bf16* x_in, float* vel_video, float* vel_audio, void* ws,
-                      size_t ws_bytes, void* stream);
+                      const h3_bf16* x_in, float* vel_video, float* vel_audio,
+                      int32_t fc2_group, void* ws, size_t ws_bytes, void* stream);
 
 /* Kernel-time accounting for diagnostics: while enabled, each kernel launch
  * of the library is bracketed by HIP events on its stream.  h3_prof_read

@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("rows,cols,group", [(7, 256, 0), (33, 5120, 0), (5, 20480, 1024),
-                                             (3, 7168, 0)])
+                                             (3, 7168, 0), (9, 4096, 512), (4, 8192, 2048),
+                                             (2, 20480, 4096)])
 def test_quantize_rows_codes_exact(rows, cols, group):
     print(f"case: quantize {rows}x{cols} group {group}", flush=True)
     x = S.normal_bf16(f"q.{rows}.{cols}", (rows, cols), 1.0)
@@ -47,14 +48,14 @@ def _i8_case(sh, L):
         S.activations(sh, field=True)
 
 
-def _run_i8(sh, ts, npt, blocks, mods, head, mf, rope, x):
+def _run_i8(sh, ts, npt, blocks, mods, head, mf, rope, x, fc2g):
     shape = B.make_shape(sh, ts, npt)
     ws = T.workspace(B.workspace_bytes(shape, ts, B.H3_WS_DIT_I8))
     qb = [B.quantize_block(T.weights_to_dev(b)) for b in blocks]
     vv = torch.empty((sh.n_video, sh.c_video), dtype=torch.float32, device="cuda")
     va = torch.empty((sh.n_audio, sh.c_audio), dtype=torch.float32, device="cuda")
     B.dit_forward_i8(shape, ts, qb, T.weights_to_dev(head), T.to_dev(np.ascontiguousarray(mods)),
-                     T.to_dev(mf), T.to_dev(rope), T.to_dev(x), vv, va, ws)
+                     T.to_dev(mf), T.to_dev(rope), T.to_dev(x), vv, va, ws, fc2_group=fc2g)
     torch.cuda.synchronize()
     # the weight codes the GPU made must be the oracle's
     for n in ("qkv", "fc2"):
@@ -64,24 +65,25 @@ def _run_i8(sh, ts, npt, blocks, mods, head, mf, rope, x):
     return vv.cpu().numpy(), va.cpu().numpy()
 
 
-def fc2_group(sh):
-    """The FC2 input is quantized per 1,024 channels when the FFN width is a
-    larger multiple of 1,024, else per row."""
-    return 1024 if sh.ffn % 1024 == 0 and sh.ffn > 1024 else 0
+def oracle_group(sh, fc2g):
+    """The oracle's FC2 grouping for the ABI's fc2_group: one group that spans
+    the whole row is the per-row form."""
+    return fc2g if fc2g and sh.ffn > fc2g else 0
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_grouped_fc2", "fasth3_tiny"])
-def test_int8_forward(name):
+@pytest.mark.parametrize("name,fc2g", [("tiny", 1024), ("tiny_grouped_fc2", 1024),
+                                       ("tiny_grouped_fc2", 0), ("fasth3_tiny", 0)])
+def test_int8_forward(name, fc2g):
     # (the int8 products need K multiples of 256: the pages' block with 8 heads of 64)
     sh = {"tiny": S.TINY, "tiny_grouped_fc2": S.TINY.replace(ffn=3072),
           "fasth3_tiny": S.FASTH3_TINY.replace(n_heads=8)}[name]
     L = 2
-    print(f"case: int8 forward {name} L={L}", flush=True)
+    print(f"case: int8 forward {name} L={L} fc2_group={fc2g}", flush=True)
     ts, npt, blocks, mods, head, mf, rope, x = _i8_case(sh, L)
-    gv, ga = _run_i8(sh, ts, npt, blocks, mods, head, mf, rope, x)
+    gv, ga = _run_i8(sh, ts, npt, blocks, mods, head, mf, rope, x, fc2g)
     qws = [O.quantize_block_int8(b) for b in blocks]
     r = O.dit_forward(sh, ts, npt, blocks, head, mods, mf, rope, x, qws=qws,
-                      fc2_group=fc2_group(sh))
+                      fc2_group=oracle_group(sh, fc2g))
     for got, ref in ((gv, r["vel_video"]), (ga, r["vel_audio"])):
         m = P.metrics(got, ref)
         assert m["cos"] >= 0.9999 and m["rel"] <= 5e-3, m
@@ -112,7 +114,7 @@ def test_int8_full_size_block_sampled_rows():
     va = torch.empty((sh.n_audio, sh.c_audio), dtype=torch.float32, device="cuda")
     B.dit_forward_i8(shape, ts, [qb], T.weights_to_dev(S.head_weights(sh)),
                      T.to_dev(mod[None]), T.to_dev(S.final_modulation(sh)), T.to_dev(rope),
-                     T.to_dev(x), vv, va, ws)
+                     T.to_dev(x), vv, va, ws, fc2_group=1024)
     torch.cuda.synchronize()
     R, H, A = sh.rows, sh.hidden, sh.attn_width
     wsh = ws.cpu().numpy()
@@ -124,7 +126,7 @@ def test_int8_full_size_block_sampled_rows():
                                      np.arange(8000, 8040), np.arange(R - 30, R)]))
     print("oracle ...", flush=True)
     r = O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows,
-                        qw=O.quantize_block_int8(w), fc2_group=fc2_group(sh))
+                        qw=O.quantize_block_int8(w), fc2_group=oracle_group(sh, 1024))
     m = P.metrics(view(lay.attn, (R, A))[rows], r["attn"])
     assert m["cos"] > 0.9999 and m["rel"] < 1e-2, ("attn", m)
     for name, off in (("x1", lay.x1), ("x2", lay.xa)):
