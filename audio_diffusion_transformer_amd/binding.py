@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libh3.so")
 
 H3_OK, H3_EINVAL, H3_EWORKSPACE, H3_EHIP, H3_EUNSUPPORTED = 0, -1, -2, -3, -4
 H3_WS_BLOCK, H3_WS_DIT, H3_WS_ATTN, H3_WS_DIT_I8 = 0, 1, 2, 3
-ABI_VERSION = 3  # must match H3_ABI_VERSION in include/h3.h
+ABI_VERSION = 4  # must match H3_ABI_VERSION in include/h3.h
 
 KERNEL_CLASSES = ["modnorm", "gemm_qkv", "heads", "route", "attn", "gemm_o", "gemm_fc1",
                   "gemm_fc2", "final", "tables", "rows_in", "time", "euler", "tokens", "quant"]
@@ -70,7 +70,7 @@ class H3WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("tables", "norm", "big", "q", "k", "vt", "qbar",
                                                "kbar", "vbar", "scores", "sel", "pooled",
                                                "attn", "x1", "xa", "xb", "q8", "qscale",
-                                               "total")] + \
+                                               "partial", "total")] + \
                [("padded_rows", ctypes.c_int32), ("n_query_tiles", ctypes.c_int32),
                 ("n_sel", ctypes.c_int32)]
 

@@ -51,6 +51,7 @@ struct Plan {
   std::vector<int> tstart, tpstart, chunk_valid, qblocks;
   h3_ws_layout lay;
   size_t off_tstart, off_tpstart, off_chunk, off_qb;
+  size_t partial_bytes = 0;
 };
 
 int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) {
@@ -186,6 +187,17 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
     const size_t ng = p.F % kFc2Group == 0 ? (size_t)(p.F / kFc2Group) : 1;
     L.qscale = take(R * (ng > 1 ? ng : 1) * f4);
   }
+  if (which != H3_WS_ATTN) {  // the products' split-K tails
+    const bool i8 = which == H3_WS_DIT_I8;
+    const int dims[4][2] = {{p.parts * p.A, p.H}, {p.H, p.A}, {p.F1, p.H}, {p.H, p.F}};
+    size_t pb = 0;
+    for (const auto& d : dims) {
+      const size_t b = gemm_partial_bytes(p.R, d[0], d[1], i8);
+      if (b > pb) pb = b;
+    }
+    p.partial_bytes = pb;
+    if (pb) L.partial = take(pb);
+  }
   L.total = off;
   L.padded_rows = p.Rp;
   L.n_query_tiles = p.nQ;
@@ -310,6 +322,16 @@ int check_block_weights(const h3_block_weights* w, int l) {
   return H3_OK;
 }
 
+// A product's epilogue arguments with the plan's split-K partial region.
+GemmEpi gemm_epi(const Plan& p, void* ws) {
+  GemmEpi e{};
+  if (p.partial_bytes) {
+    e.partial = at<void>(ws, p.lay.partial);
+    e.partial_bytes = p.partial_bytes;
+  }
+  return e;
+}
+
 // Steps 1-9 of one block; tables already uploaded.
 int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* mod,
               const float* rope, const bf16_t* x_in, bf16_t* x_out, hipStream_t st) {
@@ -326,7 +348,7 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
                         p.s.norm_eps, st));
   prof_end(H3_K_NORM, st);
 
-  GemmEpi e{};
+  GemmEpi e = gemm_epi(p, ws);
   e.bias = w->b_qkv;
   e.out = big;
   e.n_text = nt;
@@ -349,7 +371,7 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
   int rc = run_attention(p, ws, nullptr, nullptr, attn, gate, p.parts * A, p.parts * p.D, st);
   if (rc) return rc;
 
-  e = GemmEpi{};
+  e = gemm_epi(p, ws);
   e.bias = w->b_o;
   e.out = x1;
   e.res = x_in;
@@ -366,7 +388,7 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
                         p.s.norm_eps, st));
   prof_end(H3_K_NORM, st);
 
-  e = GemmEpi{};
+  e = gemm_epi(p, ws);
   e.bias = w->b_fc1;
   e.out = big;
   prof_begin(H3_K_GEMM_FC1, st);
@@ -374,7 +396,7 @@ int run_block(const Plan& p, void* ws, const h3_block_weights* w, const float* m
                      R, p.F1, H, e, st));
   prof_end(H3_K_GEMM_FC1, st);
 
-  e = GemmEpi{};
+  e = gemm_epi(p, ws);
   e.bias = w->b_fc2;
   e.out = x_out;
   e.res = x1;
@@ -418,7 +440,7 @@ int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const fl
                           nullptr, st));
   prof_end(H3_K_NORM, st);
 
-  GemmEpi e{};
+  GemmEpi e = gemm_epi(p, ws);
   e.bias = w->b_qkv;
   e.out = big;
   e.n_text = nt;
@@ -445,7 +467,7 @@ int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const fl
   prof_begin(H3_K_QUANT, st);
   H3_TRY(launch_quant_rows(attn, R, A, A, q8, qs, st));
   prof_end(H3_K_QUANT, st);
-  e = GemmEpi{};
+  e = gemm_epi(p, ws);
   e.bias = w->b_o;
   e.out = x1;
   e.res = x_in;
@@ -464,7 +486,7 @@ int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const fl
                           nullptr, st));
   prof_end(H3_K_NORM, st);
 
-  e = GemmEpi{};
+  e = gemm_epi(p, ws);
   e.bias = w->b_fc1;
   e.out = big;
   e.a_scale = qs;
@@ -478,7 +500,7 @@ int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const fl
   prof_begin(H3_K_QUANT, st);
   H3_TRY(launch_quant_rows(big, R, F, grouped ? kFc2Group : F, q8, qs, st));
   prof_end(H3_K_QUANT, st);
-  e = GemmEpi{};
+  e = gemm_epi(p, ws);
   e.bias = w->b_fc2;
   e.out = x_out;
   e.res = x1;

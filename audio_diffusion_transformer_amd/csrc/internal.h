@@ -33,7 +33,14 @@ struct GemmEpi {
   int n_text, n_prefix; // row segment boundaries
   const float* a_scale; // int8 products: [M] row scales of A
   const float* b_scale; // int8 products: [N] row scales of B (output columns)
+  void* partial;         // null, or workspace for the split-K tail's partial sums
+  size_t partial_bytes;  // its size
+  int n_main, split;     // set by the launcher: whole tiles, ways of the split tail
 };
+// a launch round: one 256x256 tile per CU; a tail tile is split at most 16 ways
+constexpr int kGemmRound = 256, kGemmMaxSplit = 16;
+// bytes of partial sums the split-K tail of this product uses (<= 64 MB; 0: no split)
+size_t gemm_partial_bytes(int M, int N, int K, bool i8);
 bool gemm_shape_ok(int M, int N, int K);
 bool gemm_i8_shape_ok(int M, int N, int K);
 hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, int K,

@@ -119,7 +119,19 @@ __device__ __forceinline__ int seg_of(int row, int n_text, int n_prefix) {
 // I8: int8 operands (v_mfma_i32_16x16x64_i8, 64 k-values per product, 128
 // per stage) with exact int32 sums, scaled in the epilogue by the row scale
 // of A and the column scale of B: acc_f = (float)acc * a_scale[row] * b_scale[col].
-template <int EPI, bool I8>
+//
+// Split-K tail (MODE).  The tiles of the last, partly filled round would
+// leave most CUs idle; instead the first ep.n_main workgroups of the launch
+// (MODE_MAIN) cover the full rounds, and the remaining `tail` tiles are each
+// split into S ranges of K, one workgroup per range, which writes its raw sums
+// (fp32, or int32 for int8) to a workspace slot in the thread layout of the
+// accumulators (a thread's 128 sums are one column of 16-byte vectors).  A
+// second launch (MODE_REDUCE) adds a tile's S slots in a fixed order and runs
+// the epilogue, one workgroup per tile and block row i of the accumulators
+// (16 rows of each wave's 128), so that eight workgroups share a tile's reads.
+enum { MODE_MAIN = 0, MODE_REDUCE = 1 };
+
+template <int EPI, bool I8, int MODE>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A,
                                                       const void* __restrict__ B, int M,
                                                       int N, int K, GemmEpi ep) {
@@ -129,8 +141,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   const int nb = gridDim.x, bid = blockIdx.x;
-  const int q8 = nb >> 3, r8 = nb & 7, xcd = bid & 7, idx = bid >> 3;
-  const int lin = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+  int lin, slot = 0, part = 0, ib = 0;
+  bool is_part = false;
+  if constexpr (MODE == MODE_MAIN) {
+    if (bid < ep.n_main) {  // XCD-aware: consecutive tiles on one XCD
+      const int nm = ep.n_main;
+      const int q8 = nm >> 3, r8 = nm & 7, xcd = bid & 7, idx = bid >> 3;
+      lin = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+    } else {  // tail tile t = slot / S, K range slot % S
+      is_part = true;
+      slot = bid - ep.n_main;
+      part = slot % ep.split;
+      lin = ep.n_main + slot / ep.split;
+    }
+  } else {
+    slot = (bid >> 3) * ep.split;  // the tile's first slot
+    ib = bid & 7;                  // block row of the accumulators
+    lin = ep.n_main + (bid >> 3);
+  }
+  (void)nb;
   constexpr int GROUP = 8;
   const int per_group = GROUP * tiles_n;
   const int g = lin / per_group;
@@ -221,53 +250,83 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
   };
 
   const int KT = rowb / STAGE_BYTES;  // >= 2
-  issue(0);
-  if (grp == 1) {
-    issue(1);
-    __builtin_amdgcn_s_waitcnt(H3_VMCNT(8));  // stage 0 landed; stage 1 may be in flight
-  } else {
-    __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
-  }
-  phase_barrier();
-  if (grp == 1) phase_barrier();  // the second group runs one phase behind
-  for (int s = 0; s < KT; ++s) {
-    // memory phase
-    if (grp == 0 && s + 1 < KT) issue(s + 1);
-    read_frags(s);
-    __builtin_amdgcn_s_waitcnt(H3_LGKMCNT0);
+  // stages [k0, k1): all of K, or one of the S ranges of a split tile (>= 2 stages)
+  const int k0 = is_part ? part * KT / ep.split : 0;
+  const int k1 = is_part ? (part + 1) * KT / ep.split : KT;
+  if constexpr (MODE == MODE_MAIN) {
+    issue(k0);
     if (grp == 1) {
-      if (s + 2 < KT) {
-        issue(s + 2);
-        __builtin_amdgcn_s_waitcnt(H3_VMCNT(8));  // this wave's half of stage s+1 has landed
-      } else {
-        __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
-      }
+      issue(k0 + 1);
+      __builtin_amdgcn_s_waitcnt(H3_VMCNT(8));  // stage k0 landed; stage k0+1 may be in flight
+    } else {
+      __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
     }
     phase_barrier();
-    // MFMA phase
-    products();
-    if (grp == 0 && s + 1 < KT) __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
-    phase_barrier();
+    if (grp == 1) phase_barrier();  // the second group runs one phase behind
+    for (int s = k0; s < k1; ++s) {
+      // memory phase
+      if (grp == 0 && s + 1 < k1) issue(s + 1);
+      read_frags(s);
+      __builtin_amdgcn_s_waitcnt(H3_LGKMCNT0);
+      if (grp == 1) {
+        if (s + 2 < k1) {
+          issue(s + 2);
+          __builtin_amdgcn_s_waitcnt(H3_VMCNT(8));  // this wave's half of stage s+1 has landed
+        } else {
+          __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+        }
+      }
+      phase_barrier();
+      // MFMA phase
+      products();
+      if (grp == 0 && s + 1 < k1) __builtin_amdgcn_s_waitcnt(H3_VMCNT(0));
+      phase_barrier();
+    }
+    if (grp == 0) phase_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
-  if (grp == 0) phase_barrier();
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if (MODE == MODE_MAIN && is_part) {  // raw sums of this K range to slot `slot`
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(ep.partial) + (size_t)slot * 32 * 512 + tid;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dst[(i * 4 + j) * 512] = I8 ? __builtin_bit_cast(u32x4_t, acci[i][j])
+                                    : __builtin_bit_cast(u32x4_t, acc[i][j]);
+    return;
+  }
+  if constexpr (MODE == MODE_REDUCE) {  // block row ib of the tile's S slots, in order
+    const u32x4_t* src =
+        reinterpret_cast<const u32x4_t*>(ep.partial) + ((size_t)slot * 32 + ib * 4) * 512 + tid;
+#pragma unroll 4
+    for (int p = 0; p < ep.split; ++p) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4_t v = src[((size_t)p * 32 + j) * 512];
+        if constexpr (I8) acci[0][j] += __builtin_bit_cast(i32x4_t, v);
+        else acc[0][j] += __builtin_bit_cast(f32x4_t, v);
+      }
+    }
+  }
+  // block rows in the epilogue: all 8, or row ib (held in acc[0]) when reducing
+  constexpr int NI = MODE == MODE_REDUCE ? 1 : 8;
 
   // ---- epilogue ----
   // Accumulator element e of block (i, j) in lane l sits at row 4(l/16) + e,
   // column l%16 of that 16x16 block.  Each wave rounds its 128x64 sub-tile into
   // its own 16 KB of LDS, then writes it back in 16-byte chunks.
   if constexpr (I8) {  // int32 sums -> fp32 with the row and column scales
-    float sa[8][4], sb[4];
+    float sa[NI][4], sb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        sa[i][e] = ep.a_scale[min(m0 + wm * 128 + i * 16 + 4 * q4 + e, M - 1)];
+        sa[i][e] = ep.a_scale[min(m0 + wm * 128 + (i + ib) * 16 + 4 * q4 + e, M - 1)];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sb[j] = ep.b_scale[n0 + wn * 64 + j * 16 + l16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -285,10 +344,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
       const int ncol = n0 + wn * 64 + jj * 32 + l16;
       const float bg = bf2f(ep.bias[ncol]), bu = bf2f(ep.bias[ncol + 16]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = i * 16 + 4 * q4 + e;
+          const int r = (i + ib) * 16 + 4 * q4 + e;
           const float g = bf2f(f2bf(acc[i][2 * jj][e] + bg));
           const float u = bf2f(f2bf(acc[i][2 * jj + 1][e] + bu));
           const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
@@ -299,8 +358,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
     __builtin_amdgcn_wave_barrier();
     const int NO = N / 2;  // output width
 #pragma unroll 4
-    for (int t = 0; t < 8; ++t) {
-      const int q = t * 64 + lane;
+    for (int t = 0; t < NI; ++t) {  // 16 rows per t
+      const int q = (t + ib) * 64 + lane;
       const int r = q >> 2, c8 = (q & 3) * 8;
       const int row = m0 + wm * 128 + r;
       if (row >= M) continue;
@@ -314,10 +373,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
   for (int j = 0; j < 4; ++j) {
     const float bias = bf2f(ep.bias[n0 + wn * 64 + j * 16 + l16]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = i * 16 + 4 * q4 + e;
+        const int r = (i + ib) * 16 + 4 * q4 + e;
         float v = acc[i][j][e] + bias;
         if constexpr (EPI == EPI_BIAS_GELU) v = gelu_erf(v);
         st[r * 64 + j * 16 + l16] = f2bf(v);
@@ -326,8 +385,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll 4
-  for (int t = 0; t < 16; ++t) {
-    const int q = t * 64 + lane;
+  for (int t = 0; t < 2 * NI; ++t) {  // 8 rows per t
+    const int q = (t + 2 * ib) * 64 + lane;
     const int r = q >> 3, c8 = (q & 7) * 8;
     const int row = m0 + wm * 128 + r;
     if (row >= M) continue;
@@ -549,30 +608,79 @@ bool gemm_i8_shape_ok(int M, int N, int K) {
          (long long)M * K < (1ll << 31) && (long long)N * K < (1ll << 31);
 }
 
-template <bool I8>
+template <bool I8, int MODE>
 static void launch_epi(int epi, dim3 grid, dim3 block, const void* A, const void* B, int M, int N,
                        int K, const GemmEpi& ep, hipStream_t s) {
   switch (epi) {
     case EPI_BIAS:
-      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS, I8>), grid, block, 0, s, A, B, M, N, K, ep);
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS, I8, MODE>), grid, block, 0, s, A, B, M, N, K, ep);
       break;
     case EPI_BIAS_GELU:
-      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_GELU, I8>), grid, block, 0, s, A, B, M, N, K, ep);
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_GELU, I8, MODE>), grid, block, 0, s, A, B, M, N, K,
+                         ep);
       break;
     case EPI_BIAS_SWIGLU:
-      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_SWIGLU, I8>), grid, block, 0, s, A, B, M, N, K, ep);
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_SWIGLU, I8, MODE>), grid, block, 0, s, A, B, M, N,
+                         K, ep);
       break;
     default:
-      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_RESGATE, I8>), grid, block, 0, s, A, B, M, N, K, ep);
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BIAS_RESGATE, I8, MODE>), grid, block, 0, s, A, B, M, N,
+                         K, ep);
       break;
   }
 }
 
+// Ways the tiles of the last round are split along K: 0 (no split) unless
+// that round is at most half filled; each range keeps >= 2 stages.
+static int tail_split(int M, int N, int K, int es) {
+  const int tiles = ((M + BM - 1) / BM) * (N / BN);
+  const int KT = K * es / STAGE_BYTES;
+  const int tail = tiles % kGemmRound;
+  if (tail == 0 || 2 * tail > kGemmRound) return 0;
+  int S = kGemmRound / tail;
+  if (S > kGemmMaxSplit) S = kGemmMaxSplit;
+  if (S > KT / 2) S = KT / 2;
+  return S < 2 ? 0 : S;
+}
+
+size_t gemm_partial_bytes(int M, int N, int K, bool i8) {
+  const int S = tail_split(M, N, K, i8 ? 1 : 2);
+  const int tail = (((M + BM - 1) / BM) * (N / BN)) % kGemmRound;
+  return (size_t)S * tail * BM * BN * 4;
+}
+
+// The full rounds of tiles and, when the last round is at most half filled
+// and the workspace holds its partial sums, that round split along K, in one
+// launch; then the reduction of the split tiles.
+template <bool I8>
+static hipError_t launch_split(int epi, const void* A, const void* B, int M, int N, int K,
+                               const GemmEpi& ep_in, hipStream_t s) {
+  const int tiles = ((M + BM - 1) / BM) * (N / BN);
+  const int tail = tiles % kGemmRound;
+  int S = tail_split(M, N, K, I8 ? 1 : 2);
+  if (!ep_in.partial || gemm_partial_bytes(M, N, K, I8) > ep_in.partial_bytes) S = 0;
+  GemmEpi ep = ep_in;
+  if (S < 2) {
+    ep.n_main = tiles;
+    ep.split = 1;
+    launch_epi<I8, MODE_MAIN>(epi, dim3(tiles), dim3(512), A, B, M, N, K, ep, s);
+    return hipGetLastError();
+  }
+  ep.n_main = tiles - tail;
+  ep.split = S;
+  launch_epi<I8, MODE_MAIN>(epi, dim3(ep.n_main + tail * S), dim3(512), A, B, M, N, K, ep, s);
+  launch_epi<I8, MODE_REDUCE>(epi, dim3(tail * 8), dim3(512), A, B, M, N, K, ep, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int epi, const bf16_t* A, const bf16_t* B, int M, int N, int K,
                        const GemmEpi& ep, hipStream_t s) {
-  const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  launch_epi<false>(epi, dim3(tiles), dim3(512), A, B, M, N, K, ep, s);
-  return hipGetLastError();
+  return launch_split<false>(epi, A, B, M, N, K, ep, s);
+}
+
+hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* B, int M, int N, int K,
+                          const GemmEpi& ep, hipStream_t s) {
+  return launch_split<true>(epi, A, B, M, N, K, ep, s);
 }
 
 bool gemm_i8g_shape_ok(int M, int N, int K, int G) {
@@ -584,13 +692,6 @@ hipError_t launch_gemm_i8g_resgate(const int8_t* A, const int8_t* B, int M, int 
   if (G != kFc2Group) return hipErrorInvalidValue;
   const int tiles = ((M + BMG - 1) / BMG) * (N / BN);
   hipLaunchKernelGGL((k_gemm_i8g<kFc2Group>), dim3(tiles), dim3(512), 0, s, A, B, M, N, K, ep);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* B, int M, int N, int K,
-                          const GemmEpi& ep, hipStream_t s) {
-  const int tiles = ((M + BM - 1) / BM) * (N / BN);
-  launch_epi<true>(epi, dim3(tiles), dim3(512), A, B, M, N, K, ep, s);
   return hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ enum {
 
 enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2, H3_WS_DIT_I8 = 3 };
 
-#define H3_ABI_VERSION 3
+#define H3_ABI_VERSION 4
 
 typedef struct {
   int32_t n_text, n_audio, n_video;  /* packed in this order */
@@ -134,6 +134,7 @@ typedef struct {
   size_t tables, norm, big, q, k, vt, qbar, kbar, vbar, scores, sel, pooled, attn, x1;
   size_t xa, xb;         /* residual ping-pong of h3_dit_forward (0 if unused) */
   size_t q8, qscale;     /* int8 forward: activation codes [R][max(H, A, F)], row scales [R] */
+  size_t partial;        /* products: partial sums of a split last round (0 if unused) */
   size_t total;
   int32_t padded_rows;   /* Rp */
   int32_t n_query_tiles; /* nQ = n_tiles - n_prefix_tiles */

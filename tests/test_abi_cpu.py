@@ -35,7 +35,48 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.h3_abi_version() == 3
+    """The header, the library and the binding agree on the ABI version."""
+    src = open(os.path.join(ROOT, "include", "h3.h")).read()
+    declared = int(re.search(r"#define H3_ABI_VERSION (\d+)", src).group(1))
+    assert lib.h3_abi_version() == declared == B.ABI_VERSION
+
+
+def _split_ways(M, N, K, es):
+    """Host rule for a product's split-K tail: the last round of 256x256 tiles
+    (one per CU) is split along K when it is at most half filled, into at most
+    16 ranges of >= 2 stages of 128 bytes."""
+    tiles = -(-M // 256) * (N // 256)
+    tail = tiles % 256
+    if tail == 0 or 2 * tail > 256:
+        return 0, tail
+    s = min(256 // tail, 16, K * es // 128 // 2)
+    return (s if s >= 2 else 0), tail
+
+
+@pytest.mark.parametrize("name", ["TINY", "MID", "FULL", "FASTH3", "FASTH3_TINY"])
+def test_split_tail_region(lib, name):
+    """The workspace holds the partial sums of the largest split-K tail of the
+    block's four products (and none for the attention-only workspace)."""
+    sh = getattr(S, name)
+    shape, ts = _shape(sh)
+    R, H, A, F = sh.rows, sh.hidden, sh.attn_width, sh.ffn
+    F1 = 2 * F if sh.mlp else F
+    dims = [((3 + sh.gate) * A, H), (H, A), (F1, H), (H, F)]
+    for which, es in ((B.H3_WS_BLOCK, 2), (B.H3_WS_DIT, 2), (B.H3_WS_DIT_I8, 1)):
+        if which == B.H3_WS_DIT_I8 and any(d[1] % 256 for d in dims):
+            continue
+        want = 0
+        for N, K in dims:
+            s, tail = _split_ways(R, N, K, es)
+            want = max(want, s * tail * 256 * 256 * 4)
+        lay = B.workspace_layout(shape, ts, which)
+        if want:
+            assert lay.partial % 256 == 0 and lay.partial + want <= lay.total
+            assert lay.partial >= max(lay.x1, lay.xb, lay.qscale)
+        else:
+            assert lay.partial == 0
+        assert want <= 64 << 20
+    assert B.workspace_layout(shape, ts, B.H3_WS_ATTN).partial == 0
 
 
 def _shape(sh):
