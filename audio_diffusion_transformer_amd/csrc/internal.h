@@ -38,7 +38,7 @@ struct GemmEpi {
   int n_main, split;     // set by the launcher: whole tiles, ways of the split tail
 };
 // a launch round: one 256x256 tile per CU; a tail tile is split at most 16 ways
-constexpr int kGemmRound = 256, kGemmMaxSplit = 16;
+constexpr int kGemmRound = 256, kGemmMaxSplit = 16, kGemmSplitMinStages = 36;
 // bytes of partial sums the split-K tail of this product uses (<= 64 MB; 0: no split)
 size_t gemm_partial_bytes(int M, int N, int K, bool i8);
 bool gemm_shape_ok(int M, int N, int K);

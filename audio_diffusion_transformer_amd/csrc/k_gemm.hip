@@ -631,7 +631,10 @@ static void launch_epi(int epi, dim3 grid, dim3 block, const void* A, const void
 }
 
 // Ways the tiles of the last round are split along K: 0 (no split) unless
-// that round is at most half filled; each range keeps >= 2 stages.
+// that round is at most half filled; each range keeps >= 2 stages.  The split
+// costs about 50 us whatever its size (the partial sums' round trip through
+// HBM and the reduction launch), some 36 stages of a tile's K loop, so it is
+// taken only when it shortens the last round by at least that much.
 static int tail_split(int M, int N, int K, int es) {
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   const int KT = K * es / STAGE_BYTES;
@@ -640,7 +643,8 @@ static int tail_split(int M, int N, int K, int es) {
   int S = kGemmRound / tail;
   if (S > kGemmMaxSplit) S = kGemmMaxSplit;
   if (S > KT / 2) S = KT / 2;
-  return S < 2 ? 0 : S;
+  if (S < 2 || KT - (KT + S - 1) / S < kGemmSplitMinStages) return 0;
+  return S;
 }
 
 size_t gemm_partial_bytes(int M, int N, int K, bool i8) {

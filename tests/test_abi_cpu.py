@@ -44,13 +44,16 @@ def test_abi_version(lib):
 def _split_ways(M, N, K, es):
     """Host rule for a product's split-K tail: the last round of 256x256 tiles
     (one per CU) is split along K when it is at most half filled, into at most
-    16 ranges of >= 2 stages of 128 bytes."""
+    16 ranges of >= 2 stages of 128 bytes, when that saves >= 36 stages."""
     tiles = -(-M // 256) * (N // 256)
     tail = tiles % 256
     if tail == 0 or 2 * tail > 256:
         return 0, tail
-    s = min(256 // tail, 16, K * es // 128 // 2)
-    return (s if s >= 2 else 0), tail
+    kt = K * es // 128
+    s = min(256 // tail, 16, kt // 2)
+    if s < 2 or kt - -(-kt // s) < 36:
+        return 0, tail
+    return s, tail
 
 
 @pytest.mark.parametrize("name", ["TINY", "MID", "FULL", "FASTH3", "FASTH3_TINY"])
