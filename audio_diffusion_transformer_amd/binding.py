@@ -138,6 +138,7 @@ def lib():
                                ctypes.POINTER(ctypes.c_double)]
     L.h3_prof_kernel_name.argtypes = [ctypes.c_int32]
     L.h3_prof_kernel_name.restype = ctypes.c_char_p
+    L.h3_calibrate_mfma.argtypes = [_vp, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
     for f in (L.h3_workspace_layout, L.h3_block_forward, L.h3_dit_forward, L.h3_routed_attn,
               L.h3_rows_in, L.h3_modulation, L.h3_denoise, L.h3_dit_forward_tr,
               L.h3_quantize_rows, L.h3_dit_forward_i8,
@@ -375,6 +376,15 @@ def dit_forward_i8(shape, tile_start, blocks, heads, mod, mod_final, rope, x_in,
                                    _ptr(mod_final), _ptr(rope), _ptr(x_in), _ptr(vel_video),
                                    _ptr(vel_audio), int(fc2_group), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def calibrate_mfma(operands, n_blocks, iters, sink, stream=None):
+    """Matrix-core calibration (h3_calibrate_mfma): operands a device tensor of
+    random bf16 data, sink a device tensor of >= 256 floats.  Returns the FLOP
+    the call performs; the caller times it."""
+    _check(lib().h3_calibrate_mfma(_ptr(operands), operands.numel() * operands.element_size(),
+                                   n_blocks, iters, _ptr(sink), _stream(stream)))
+    return n_blocks * 4 * iters * 16 * 16384
 
 
 def prof_enable(on=True):

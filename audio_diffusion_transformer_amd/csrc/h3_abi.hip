@@ -1096,6 +1096,16 @@ int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms) {
   return H3_OK;
 }
 
+int h3_calibrate_mfma(const void* operands, size_t operand_bytes, int32_t n_blocks,
+                      int32_t iters, float* sink, void* stream) {
+  if (!operands || !sink) return fail(H3_EINVAL, "operands or sink is NULL");
+  if (operand_bytes < 16 || operand_bytes % 16) return fail(H3_EINVAL, "operand_bytes must be a positive multiple of 16");
+  if (n_blocks < 1 || n_blocks > (1 << 20) || iters < 1) return fail(H3_EINVAL, "n_blocks or iters out of range");
+  H3_TRY(launch_calib_mfma(operands, operand_bytes, n_blocks, iters, sink,
+                           static_cast<hipStream_t>(stream)));
+  return H3_OK;
+}
+
 const char* h3_prof_kernel_name(int32_t cls) {
   static const char* names[H3_K_COUNT] = {"modnorm", "gemm_qkv", "heads", "route", "attn",
                                           "gemm_o", "gemm_fc1", "gemm_fc2", "final", "tables",

@@ -112,6 +112,9 @@ struct AttnArgs {
   int nh, Rp, A, nT, npt, nQ, nsel, nqb, nqb_dense, n_prefix_chunks, n_chunks;
 };
 bool attn_shape_ok(int n_chunks, int nsel);
+// matrix-core calibration: n_blocks x 4 waves x iters x 16 bf16 products
+hipError_t launch_calib_mfma(const void* operands, size_t bytes, int n_blocks, int iters,
+                             float* sink, hipStream_t s);
 hipError_t launch_attn(int head_dim, const AttnArgs& a, hipStream_t s);
 
 // ---- output heads: vel[r][c] = z[r] . W[c] + b[c] (fp32 out) --------------------

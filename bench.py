@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--attn-sweep", action="store_true",
                     help="only time h3_routed_attn at 15,435 rows x 40 heads x 128 over tile "
                          "size {32, 64, 128} x top-k {8, 32, all}; one JSON line per case")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only measure what the products and the row kernels can reach on this "
+                         "GPU: an MFMA-only loop (h3_calibrate_mfma, bf16 16x16x32 on random "
+                         "operands) and a 1 GiB device copy")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) three "
                          "times, to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -256,6 +260,49 @@ def attn_sweep():
                   flush=True)
 
 
+def calibrate():
+    """The matrix-core rate an MFMA-only loop reaches here (the clock under a
+    sustained MFMA load sits below the one the published peak is quoted at)
+    and the bandwidth of a plain device copy; median of 7 timed calls after 2
+    warm-up calls, HIP events on the launch stream."""
+    import torch
+    from audio_diffusion_transformer_amd import binding as B
+    torch.manual_seed(0)
+    ops = torch.randn(8 << 20, device="cuda").to(torch.bfloat16)   # 16 MiB of random bf16
+    sink = torch.zeros(256, device="cuda")
+    stream = torch.cuda.current_stream()
+    nb, iters = 256 * 8, 4000
+
+    def timed(fn, reps=7, warm=2):
+        for _ in range(warm):
+            fn()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return sorted(out)[len(out) // 2]
+
+    flop = nb * 4 * iters * 16 * 16384
+    ms = timed(lambda: B.calibrate_mfma(ops, nb, iters, sink, stream=stream))
+    n = 1 << 28  # 1 GiB of fp32 each way
+    src = torch.empty(n, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    cms = timed(lambda: dst.copy_(src))
+    line = {"calibration": {
+        "mfma_bf16_tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+        "mfma_frac_of_published": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "mfma_call_ms": round(ms, 3), "mfma_flop": flop,
+        "copy_gbs": round(2 * 4 * n / (cms * 1e-3) / 1e9, 1),
+        "copy_frac_of_published": round(2 * 4 * n / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "copy_call_ms": round(cms, 3), "copy_bytes": 2 * 4 * n,
+        "device": torch.cuda.get_device_name(0)}}
+    print(json.dumps(line), flush=True)
+
+
 def copy_calibration():
     import torch
     n = 1 << 28                      # 2^28 fp32 = 1 GiB each way
@@ -343,6 +390,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.calibrate:
+        calibrate()
         return
     if args.attn_sweep:
         attn_sweep()

@@ -332,6 +332,19 @@ int h3_prof_enable(int on);
 int h3_prof_read(int32_t cls, int64_t* launches, double* total_ms);
 const char* h3_prof_kernel_name(int32_t cls);
 
+/* Calibration of the matrix cores (measurement only, not a step of the
+ * method): n_blocks workgroups of 4 waves, each wave running iters rounds of
+ * 16 independent bf16 products v_mfma_f32_16x16x32_bf16 (16,384 FLOP each) on
+ * operands read from `operands` (device memory holding random bf16 data,
+ * operand_bytes >= 16 and a multiple of 16), so one call performs
+ * n_blocks * 4 * iters * 16 * 16,384 FLOP; the caller times it on `stream`.
+ * Under such a load the clock settles below the one the published peak is
+ * quoted at; the result is the rate the products can reach here.  sink:
+ * device, 256 floats (written only if the sums hit a value they cannot
+ * reach).  H3_EINVAL on null pointers or sizes out of range. */
+int h3_calibrate_mfma(const void* operands, size_t operand_bytes, int32_t n_blocks,
+                      int32_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

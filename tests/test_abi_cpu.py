@@ -245,3 +245,13 @@ def test_token_reduction_validates_before_launch(lib):
     assert call(bad.c) == B.H3_EINVAL and "reduced shape" in B.last_error()
     assert lib.h3_dit_forward_tr(ctypes.byref(shape), 4, tp, None, w, ctypes.byref(hw), None,
                                  None, None, None, None, None, None, 0, None) == B.H3_EINVAL
+
+
+def test_calibration_validates_before_launch(lib):
+    rc = lib.h3_calibrate_mfma(None, 1 << 20, 8, 10, ctypes.c_void_p(256), None)
+    assert rc == B.H3_EINVAL and "NULL" in B.last_error()
+    rc = lib.h3_calibrate_mfma(ctypes.c_void_p(256), 24, 8, 10, ctypes.c_void_p(256), None)
+    assert rc == B.H3_EINVAL and "multiple of 16" in B.last_error()
+    rc = lib.h3_calibrate_mfma(ctypes.c_void_p(256), 1 << 20, 0, 10, ctypes.c_void_p(256), None)
+    assert rc == B.H3_EINVAL
+

@@ -3,7 +3,9 @@
 and k, the top-k rule cases, and routed-with-all-tiles equals dense."""
 import numpy as np
 import pytest
+import torch
 
+from audio_diffusion_transformer_amd import binding as B
 from audio_diffusion_transformer_amd import synth as S
 from oracle import h3_oracle as O
 
@@ -146,3 +148,15 @@ def test_full_size_all_tiles_equals_dense(tile):
     routed = G.run_routed(sh, ts, npt, q, k, v)
     dense = _dense_equivalent(sh, ts, npt, q, k, v)
     np.testing.assert_array_equal(routed["out_bits"], dense["out_bits"])
+
+
+def test_calibration_probe_runs_and_stores_nothing():
+    """The matrix-core calibration call (measurement only) runs its products and
+    leaves the sink untouched (its sums cannot reach the trigger value)."""
+    print("case: h3_calibrate_mfma, 16 workgroups x 50 rounds", flush=True)
+    ops = torch.randn(1 << 16, device="cuda").to(torch.bfloat16)
+    sink = torch.zeros(256, device="cuda")
+    flop = B.calibrate_mfma(ops, 16, 50, sink)
+    torch.cuda.synchronize()
+    assert flop == 16 * 4 * 50 * 16 * 16384
+    assert not sink.any()
