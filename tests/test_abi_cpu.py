@@ -255,3 +255,22 @@ def test_calibration_validates_before_launch(lib):
     rc = lib.h3_calibrate_mfma(ctypes.c_void_p(256), 1 << 20, 0, 10, ctypes.c_void_p(256), None)
     assert rc == B.H3_EINVAL
 
+
+@pytest.mark.parametrize("n_video,top_k,hidden,code", [
+    (130944, 512, 256, B.H3_OK),                  # 2,048 tiles, 4,096 chunks, top-k 512
+    (131008, 512, 256, B.H3_EUNSUPPORTED),        # 2,049 tiles (and 4,098 chunks)
+    (130944, 513, 256, B.H3_EUNSUPPORTED),        # 513 selected tiles
+    (1024, 4, 8192, B.H3_OK),                     # the widest hidden the row kernels hold
+    (1024, 4, 8448, B.H3_EUNSUPPORTED),
+])
+def test_size_limits_on_host(lib, n_video, top_k, hidden, code):
+    """The plan accepts the kernels' limits and refuses one step beyond, on the
+    host (the limits size LDS tables and per-lane score registers)."""
+    sh = S.Shape(64, 64, n_video, hidden, 4, 64, 256, tile=64, top_k=top_k)
+    shape, ts = _shape(sh)
+    lay = B.H3WsLayout()
+    rc = lib.h3_workspace_layout(ctypes.byref(shape),
+                                 ts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 B.H3_WS_BLOCK, ctypes.byref(lay))
+    assert rc == code, B.last_error()
+

@@ -140,6 +140,8 @@ def _ragged_tiles(n_text, n_audio, n_video, sizes):
     # a single video tile; a single row of video
     dict(sh=S.Shape(10, 10, 64, 256, 2, 128, 256, top_k=1), sizes=None),
     dict(sh=S.Shape(10, 10, 1, 256, 2, 128, 256, top_k=1), sizes=None),
+    # no video rows: every row dense, no routing
+    dict(sh=S.Shape(64, 100, 0, 256, 4, 64, 256, top_k=2), sizes=None),
 ])
 def test_edge_shapes(case):
     sh = case["sh"]
@@ -154,3 +156,43 @@ def test_no_rope_table():
     sh = S.TINY
     ts, npt, w, mod, rope, x = _inputs(sh)
     _check_block(sh, ts, npt, w, mod, None, x)
+
+
+def test_block_at_size_limits():
+    """The kernels' limits at once: 2,048 tiles (the routing's 64 lanes x 32
+    scores), 4,096 key chunks of 32 padded rows (131,072 rows: the attention's
+    chunk table) and top-k 512 (its selection table).  q, k, v and the routing
+    are compared for every row, the rest on sampled rows (dense rows attend all
+    131,072 keys, video rows the prefix and 512 tiles)."""
+    sh = S.Shape(64, 64, 130944, 256, 4, 64, 256, tile=64, top_k=512)
+    print("case: block at the size limits (2048 tiles, 4096 chunks, top-k 512)", flush=True)
+    ts, npt, w, mod, rope, x = _inputs(sh)
+    assert len(ts) - 1 == 2048
+    run = G.BlockRun(sh, ts, npt, w, mod, rope, x)
+    run.run()
+    g = run.read()
+    R = sh.rows
+    rows = np.unique(np.concatenate([np.arange(0, 3), np.arange(126, 130), np.arange(60000, 60070),
+                                     np.arange(R - 70, R)]))
+    print("oracle ...", flush=True)
+    r = O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows)
+    c = G.Checks("block at the size limits")
+    c.close("q", g["q"], r["q"], atol=2 ** -5)
+    c.close("k", g["k"], r["k"], atol=2 ** -5)
+    # 34M values of v: a 1-spacing flip of a large n1 value (spacing 2^-6 for
+    # |n1| in [2, 4)) times a weight moves a product by up to ~2^-9, as in the
+    # full-size test (seen here on 0.006% of the values)
+    c.close("v", g["v"], r["v"], atol=2 ** -9)
+    c.true("scores", np.max(np.abs(g["scores"] - r["scores"])) < 1e-3,
+           f"{np.max(np.abs(g['scores'] - r['scores'])):.3g}")
+    checked, bad, skipped = P.selection_agrees(g["sel"], r["sel"], r["scores"], npt, sh.top_k)
+    c.true("sel", bad == 0 and checked > 0, f"checked {checked} bad {bad} skipped {skipped}")
+    c.true("sel order", bool(np.all(np.diff(g["sel"], axis=-1) > 0)))
+    c.true("pooled", np.max(np.abs(g["pooled"] - r["pooled"])) < 1e-3,
+           f"{np.max(np.abs(g['pooled'] - r['pooled'])):.3g}")
+    m = P.metrics(g["attn"][rows], r["attn"])
+    c.true("attn", m["cos"] > 0.99999 and m["rel"] < 4e-3, str(m))
+    for name in ("x1", "n2", "h", "x2"):
+        c.close(name, g[name][rows], r[name], ulps=2, atol=2 ** -6, frac_1ulp=2e-2)
+    c.done()
+
