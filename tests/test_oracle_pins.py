@@ -813,3 +813,27 @@ def test_int8_block_stays_close_to_the_bf16_block():
     assert cos > 0.99, cos
     # and the int8 path really differs (it is not the bf16 path)
     assert not np.array_equal(q["x2"], ref["x2"])
+
+
+def test_quantize_weight_int8_rows_from_bf16_bits():
+    """Weight codes are per output row of the bf16 weight: row (1, -0.5, 0.25)
+    has max 1, so codes rint(127 x) = (127, -64, 32) (-63.5 rounds to even,
+    31.75 up) with scale 1/127; row (0, 0, -4) has codes (0, 0, -127), scale
+    4/127."""
+    w = bits(np.array([[1.0, -0.5, 0.25], [0.0, 0.0, -4.0]]))
+    q, s = O.quantize_weight_int8(w)
+    np.testing.assert_array_equal(q, [[127, -64, 32], [0, 0, -127]])
+    np.testing.assert_array_equal(s, np.array([1.0, 4.0], np.float32) / np.float32(127))
+
+
+def test_check_tile_map_accepts_and_refuses():
+    """A tile map covers rows [0, R) with strictly increasing starts, and its
+    prefix tiles end exactly where the text and audio rows end."""
+    ts = O.check_tile_map([0, 4, 10, 16, 20], 4, 6, 10, 2)
+    np.testing.assert_array_equal(ts, [0, 4, 10, 16, 20])
+    for bad, npt in (([0, 4, 4, 16, 20], 2),     # an empty tile
+                     ([0, 4, 10, 16, 21], 2),    # does not end at R
+                     ([1, 4, 10, 16, 20], 2),    # does not start at 0
+                     ([0, 4, 12, 16, 20], 2)):   # prefix ends inside the audio rows
+        with pytest.raises(AssertionError):
+            O.check_tile_map(bad, 4, 6, 10, npt)
