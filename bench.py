@@ -486,6 +486,21 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     print(f"timed {args.steps} forwards: {ms_per_step:.1f} ms each", file=sys.stderr, flush=True)
 
+    # ---- determinism: the first timed forward again, twice, outside the
+    # timed region; the velocities' bytes must not change ----
+    import hashlib
+
+    def vel_hash():
+        torch.cuda.synchronize()
+        h = hashlib.sha256(vv.cpu().numpy().tobytes())
+        h.update(va.cpu().numpy().tobytes())
+        return h.hexdigest()
+    forward(args.warmup)
+    h1 = vel_hash()
+    forward(args.warmup)
+    h2 = vel_hash()
+    determinism = {"runs": 2, "identical": h1 == h2, "sha256": h1[:16]}
+
     # ---- per-kernel roofline from the events of the timed region ----
     work = kernel_work(sh, ts, npt, attention_keys(sh, ts, npt))
     if tr is not None:  # mean work per launch over full-resolution and pooled blocks
@@ -563,6 +578,7 @@ def main():
                                 f"bf16 weights"),
                    "blocks": L, "rows": sh.rows, "hidden": sh.hidden, "ffn": sh.ffn,
                    "tile": sh.tile, "top_k": sh.top_k},
+        "determinism": determinism,
         "step_ms": [round(s, 2) for s in step_ms],
         "median_step_s": round(srt[len(srt) // 2] / 1e3, 5),
         "roofline": roofline,
