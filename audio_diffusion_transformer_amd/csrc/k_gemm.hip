@@ -19,17 +19,17 @@
 // Schedule (ping-pong): waves w and w + 4 share a SIMD.  Waves 0-3 (group 0)
 // and 4-7 (group 1) run the same sequence of phases one phase apart: in its
 // memory phase a wave reads the fragments of a whole stage (24 LDS reads), in
-// its MFMA phase it issues the stage's 32 products; while one wave of a SIMD
-// computes, the other reads.  All eight waves meet at a barrier between
-// phases.  Each group loads half of every stage: group 0 issues its half of
-// stage s+1 at the start of its memory phase of stage s (the buffer's last
-// readers finished a phase earlier); group 1 issues its half of stage s+2 at
-// the end of its memory phase of stage s, right after its own reads of that
-// buffer.  Both thus have two phases to land their loads before the barrier
-// that precedes the first read.  The loads are issued as inline assembly
-// (scalar base address, per-lane 32-bit offsets) so that the compiler does
-// not insert its own conservative waits for them; this kernel waits on vmcnt
-// itself.
+// its MFMA phase it issues the stage's 64 products (2 k-steps of 8x4 blocks);
+// while one wave of a SIMD computes, the other reads.  All eight waves meet at
+// a barrier between phases.  Each group loads half of every stage: group 0
+// issues its half of stage s+1 at the start of its memory phase of stage s
+// (the buffer's last readers finished a phase earlier); group 1 issues its
+// half of stage s+2 at the end of its memory phase of stage s, right after its
+// own reads of that buffer.  Both thus have two phases to land their loads
+// before the barrier that precedes the first read.  The loads are issued as
+// inline assembly (scalar base address, per-lane 32-bit offsets) so that the
+// compiler does not insert its own conservative waits for them; this kernel
+// waits on vmcnt itself.
 //
 // Workgroup ids are remapped so that each XCD (ids are dealt round-robin over
 // the 8 XCDs) works on a contiguous band of tiles; within a band tiles are
