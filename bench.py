@@ -384,7 +384,7 @@ def cpu_baseline(sh, ts, npt, n_blocks):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no "
               f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
