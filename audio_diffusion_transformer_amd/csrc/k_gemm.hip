@@ -140,7 +140,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
-  const int nb = gridDim.x, bid = blockIdx.x;
+  const int bid = blockIdx.x;
   int lin, slot = 0, part = 0, ib = 0;
   bool is_part = false;
   if constexpr (MODE == MODE_MAIN) {
@@ -159,7 +159,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
     ib = bid & 7;                  // block row of the accumulators
     lin = ep.n_main + (bid >> 3);
   }
-  (void)nb;
   constexpr int GROUP = 8;
   const int per_group = GROUP * tiles_n;
   const int g = lin / per_group;
