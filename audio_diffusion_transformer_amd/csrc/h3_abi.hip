@@ -519,8 +519,7 @@ int run_block_i8(const Plan& p, void* ws, const h3_block_weights_i8* w, const fl
   return H3_OK;
 }
 
-int check_dit_args(const Plan& p, int n_blocks, const h3_block_weights* blocks,
-                   const h3_head_weights* heads) {
+int check_dit_args(int n_blocks, const h3_block_weights* blocks, const h3_head_weights* heads) {
   int rc;
   if (n_blocks < 0) return fail(H3_EINVAL, "n_blocks < 0");
   if (n_blocks > 0 && !blocks) return fail(H3_EINVAL, "blocks is NULL");
@@ -532,7 +531,6 @@ int check_dit_args(const Plan& p, int n_blocks, const h3_block_weights* blocks,
     return fail(H3_EINVAL, "head widths must be in [1, 256]");
   if (!aligned16(heads->w_video) || !aligned16(heads->w_audio))
     return fail(H3_EINVAL, "tensor pointers must be 16-byte aligned");
-  (void)p;
   return H3_OK;
 }
 
@@ -798,7 +796,7 @@ int h3_dit_forward(const h3_shape* shape, int32_t n_blocks, const int32_t* tile_
   int rc = make_plan(shape, tile_start, H3_WS_DIT, p);
   if (rc) return rc;
   if ((rc = check_ws(p, ws, ws_bytes))) return rc;
-  if ((rc = check_dit_args(p, n_blocks, blocks, heads))) return rc;
+  if ((rc = check_dit_args(n_blocks, blocks, heads))) return rc;
   if ((n_blocks > 0 && !mod) || !mod_final || !x_in)
     return fail(H3_EINVAL, "mod, mod_final and x_in are required");
   if ((p.s.n_video > 0 && !vel_video) || (p.s.n_audio > 0 && !vel_audio))
@@ -870,7 +868,7 @@ int h3_denoise(const h3_shape* shape, int32_t n_blocks, int32_t n_steps,
   if (((uintptr_t)ws & 255) != 0) return fail(H3_EINVAL, "workspace must be 256-byte aligned");
   if (ws_bytes < dl.total)
     return fail(H3_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, dl.total);
-  if ((rc = check_dit_args(p, n_blocks, blocks, heads))) return rc;
+  if ((rc = check_dit_args(n_blocks, blocks, heads))) return rc;
   if ((rc = check_time_weights(tw, n_blocks))) return rc;
   if (!rows_w || rows_w->c_video != heads->c_video || rows_w->c_audio != heads->c_audio)
     return fail(H3_EINVAL, "rows-in weights must match the head widths");
@@ -921,7 +919,7 @@ int h3_dit_forward_tr(const h3_shape* shape, int32_t n_blocks, const int32_t* ti
   if (((uintptr_t)ws & 255) != 0) return fail(H3_EINVAL, "workspace must be 256-byte aligned");
   if (ws_bytes < tl.total)
     return fail(H3_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, tl.total);
-  if ((rc = check_dit_args(pf, n_blocks, blocks, heads))) return rc;
+  if ((rc = check_dit_args(n_blocks, blocks, heads))) return rc;
   const int r0 = tr->reduce_at, r1 = tr->restore_at;
   if (r0 < 0 || r0 > r1 || r1 > n_blocks)
     return fail(H3_EINVAL, "need 0 <= reduce_at <= restore_at <= n_blocks");
@@ -1023,7 +1021,7 @@ int h3_dit_forward_i8(const h3_shape* shape, int32_t n_blocks, const int32_t* ti
   if (n_blocks > 0 && !blocks) return fail(H3_EINVAL, "blocks is NULL");
   for (int l = 0; l < n_blocks; ++l)
     if ((rc = check_block_weights_i8(&blocks[l], l))) return rc;
-  if ((rc = check_dit_args(p, 0, nullptr, heads))) return rc;
+  if ((rc = check_dit_args(0, nullptr, heads))) return rc;
   if ((n_blocks > 0 && !mod) || !mod_final || !x_in)
     return fail(H3_EINVAL, "mod, mod_final and x_in are required");
   if ((p.s.n_video > 0 && !vel_video) || (p.s.n_audio > 0 && !vel_audio))
