@@ -4,7 +4,6 @@ import numpy as np
 import torch
 
 from audio_diffusion_transformer_amd import binding as B
-from audio_diffusion_transformer_amd import synth as S
 from audio_diffusion_transformer_amd import tensors as T
 
 import parity as P

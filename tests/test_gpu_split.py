@@ -10,7 +10,6 @@ path; the int8 forward splits its QKV, FC1 and per-row FC2 products.  The
 comparison with the oracle and the bars are those of the block and int8
 tests (same arithmetic and rounding points; only the fp32 summation order of
 the split tiles changes)."""
-import numpy as np
 import pytest
 import torch
 
