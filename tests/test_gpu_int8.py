@@ -95,12 +95,16 @@ def test_int8_forward(name, fc2g):
     assert m["cos"] >= 0.99, m
 
 
-def test_int8_full_size_block_sampled_rows():
-    """Hidden 5120, 40 x 128 heads, GELU FFN 20480 (the FC2 input in 20 groups
-    of 1,024), 15,435 rows; one int8 block through h3_dit_forward_i8 (its
-    output stays in the workspace), the oracle on sampled rows."""
-    sh = S.FULL
-    print("case: int8 full-size block (oracle on sampled rows)", flush=True)
+@pytest.mark.parametrize("name,fc2g", [("full", 1024), ("fasth3", 0)])
+def test_int8_full_size_block_sampled_rows(name, fc2g):
+    """One int8 block at full size through h3_dit_forward_i8 (its output stays
+    in the workspace), the oracle on sampled rows.  full: hidden 5120, 40 x 128
+    heads, GELU FFN 20480, the FC2 input in 20 groups of 1,024.  fasth3: the
+    pages' block (hidden 5,376, 56 x 128 heads, SwiGLU 14,336, routing gate,
+    cube tiles) with the FC2 input per row, whose out projection and FC2 (1,281
+    tiles) run their last tile as 16 ranges of K."""
+    sh = S.FULL if name == "full" else S.FASTH3
+    print(f"case: int8 full-size block {name} fc2_group={fc2g} (oracle on sampled rows)", flush=True)
     ts, npt = S.tile_map(sh)
     w = S.block_weights(sh)
     mod = S.modulation(sh)
@@ -114,7 +118,7 @@ def test_int8_full_size_block_sampled_rows():
     va = torch.empty((sh.n_audio, sh.c_audio), dtype=torch.float32, device="cuda")
     B.dit_forward_i8(shape, ts, [qb], T.weights_to_dev(S.head_weights(sh)),
                      T.to_dev(mod[None]), T.to_dev(S.final_modulation(sh)), T.to_dev(rope),
-                     T.to_dev(x), vv, va, ws, fc2_group=1024)
+                     T.to_dev(x), vv, va, ws, fc2_group=fc2g)
     torch.cuda.synchronize()
     R, H, A = sh.rows, sh.hidden, sh.attn_width
     wsh = ws.cpu().numpy()
@@ -126,12 +130,12 @@ def test_int8_full_size_block_sampled_rows():
                                      np.arange(8000, 8040), np.arange(R - 30, R)]))
     print("oracle ...", flush=True)
     r = O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows,
-                        qw=O.quantize_block_int8(w), fc2_group=oracle_group(sh, 1024))
+                        qw=O.quantize_block_int8(w), fc2_group=oracle_group(sh, fc2g))
     m = P.metrics(view(lay.attn, (R, A))[rows], r["attn"])
     assert m["cos"] > 0.9999 and m["rel"] < 1e-2, ("attn", m)
-    for name, off in (("x1", lay.x1), ("x2", lay.xa)):
+    for stage, off in (("x1", lay.x1), ("x2", lay.xa)):
         got = view(off, (R, H))[rows]
-        d = P.metrics(got - T.bf16_bits_to_f64(x)[rows], r[name] - T.bf16_bits_to_f64(x)[rows])
+        d = P.metrics(got - T.bf16_bits_to_f64(x)[rows], r[stage] - T.bf16_bits_to_f64(x)[rows])
         # the block's update of the residual (a one-step code flip moves a
         # product by about one code step, 1/127 of its row's range)
-        assert d["cos"] > 0.999 and d["rel"] < 2e-2, (name, d)
+        assert d["cos"] > 0.999 and d["rel"] < 2e-2, (stage, d)
