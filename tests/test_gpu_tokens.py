@@ -84,3 +84,44 @@ def test_token_reduction_forward(r0, r1):
     for got, ref in ((gv, r["vel_video"]), (ga, r["vel_audio"])):
         m = P.metrics(got, ref)
         assert m["cos"] >= 0.9999 and m["rel"] <= 5e-3, m
+
+
+def test_token_reduction_identity_middle_full_size():
+    """The pages' geometry at full size (15,435 rows; 7,770 pooled video rows on
+    160 cube tiles), in the launch configuration the benchmark times: with the
+    pooled block's gates zero it is the identity, so pooling, the pooled
+    stream's own tile map and the restore must give the forward over the other
+    blocks bit for bit."""
+    sh = S.FASTH3
+    print("case: token reduction at full size, identity middle block", flush=True)
+    L, r0, r1 = 3, 1, 2
+    ts, npt = S.tile_map(sh)
+    red, pairs, first = S.token_pairs(sh)
+    rts, rnpt = S.tile_map(red)
+    blocks = [S.device_block_weights(sh, block=l) for l in range(L)]
+    mods = np.stack([S.modulation(sh, block=l) for l in range(L)])
+    mods[r0:r1, :, 2, :] = 0
+    mods[r0:r1, :, 5, :] = 0
+    head = T.weights_to_dev(S.head_weights(sh))
+    mf, rope, x = T.to_dev(S.final_modulation(sh)), T.to_dev(S.rope_tables(sh)), \
+        T.to_dev(S.activations(sh, field=True))
+    shape = B.make_shape(sh, ts, npt)
+    tr = B.TokenReduction(B.make_shape(red, rts, rnpt), rts, T.to_dev(np.ascontiguousarray(pairs)),
+                          T.to_dev(S.rope_tables(red, first)), r0, r1)
+    out = []
+    for reduced in (True, False):
+        vv = torch.empty((sh.n_video, sh.c_video), dtype=torch.float32, device="cuda")
+        va = torch.empty((sh.n_audio, sh.c_audio), dtype=torch.float32, device="cuda")
+        if reduced:
+            ws = T.workspace(B.dit_forward_tr_workspace_bytes(shape, ts, tr))
+            B.dit_forward_tr(shape, ts, tr, blocks, head, T.to_dev(mods), mf, rope, x, vv, va, ws)
+        else:
+            keep = [l for l in range(L) if not r0 <= l < r1]
+            ws = T.workspace(B.workspace_bytes(shape, ts, B.H3_WS_DIT))
+            B.dit_forward(shape, ts, [blocks[l] for l in keep], head,
+                          T.to_dev(np.ascontiguousarray(mods[keep])), mf, rope, x, vv, va, ws)
+        torch.cuda.synchronize()
+        out.append((vv.cpu().numpy(), va.cpu().numpy()))
+        del ws
+    np.testing.assert_array_equal(out[0][0], out[1][0])
+    np.testing.assert_array_equal(out[0][1], out[1][1])
