@@ -95,7 +95,9 @@ def _denoise_gpu(sh, L, head, rw, tw, sig, text, lv, la, blocks):
     shape = B.make_shape(sh, ts, npt)
     ws = T.workspace(B.denoise_workspace_bytes(shape, ts, L))
     dv, da = _dev_f32(lv), _dev_f32(la)
-    B.denoise(shape, ts, [T.weights_to_dev(b) for b in blocks], T.weights_to_dev(head),
+    dev_blocks = [b if isinstance(next(iter(b.values())), torch.Tensor) else T.weights_to_dev(b)
+                  for b in blocks]
+    B.denoise(shape, ts, dev_blocks, T.weights_to_dev(head),
               {k: _dev_f32(v) for k, v in rw.items()}, T.weights_to_dev(tw), sig,
               T.to_dev(S.rope_tables(sh)), T.to_dev(text), dv, da, ws)
     torch.cuda.synchronize()
@@ -129,19 +131,29 @@ def test_denoise_passes(name):
         assert m["cos"] >= 0.9999 and m["rel"] <= 5e-3, m
 
 
-def test_denoise_constant_heads_exact():
+@pytest.mark.parametrize("name", ["small", "full"])
+def test_denoise_constant_heads_exact(name):
     """Zero head weights: the velocities are the head biases, so the GPU loop
-    must equal the float32 Euler steps exactly, on each segment's schedule."""
-    sh = S.TINY.replace(n_text=64, n_audio=64, n_video=128)
-    print("case: denoise constant heads", flush=True)
-    ts, npt, blocks, head, rw, tw, _, text, lv, la = _denoise_case(sh, 1, 3)
+    must equal the float32 Euler steps exactly, on each segment's schedule.
+    full: the default geometry (15,435 rows, hidden 5120) with two blocks in
+    the benchmark's launch configuration."""
+    if name == "small":
+        sh = S.TINY.replace(n_text=64, n_audio=64, n_video=128)
+        L = 1
+    else:
+        sh, L = S.FULL, 2
+    print(f"case: denoise constant heads {name}", flush=True)
+    ts, npt, blocks, head, rw, tw, _, text, lv, la = _denoise_case(sh, 0, 3)
+    blocks = ([S.block_weights(sh, block=l) for l in range(L)] if name == "small" else
+              [S.device_block_weights(sh, block=l) for l in range(L)])
+    tw = S.time_weights(sh, L)
     head["w_video"] = np.zeros_like(head["w_video"])
     head["w_audio"] = np.zeros_like(head["w_audio"])
     head["b_video"] = S.f32_to_bf16(np.full(sh.c_video, 0.5, np.float32))
     head["b_audio"] = S.f32_to_bf16(np.full(sh.c_audio, -0.25, np.float32))
     sig = np.array([[1.0, 1.0, 1.0], [0.5, 0.75, 0.5], [0.25, 0.5, 0.25], [0.0, 0.25, 0.0]],
                    np.float32)
-    gv, ga = _denoise_gpu(sh, 1, head, rw, tw, sig, text, lv, la, blocks)
+    gv, ga = _denoise_gpu(sh, L, head, rw, tw, sig, text, lv, la, blocks)
     ev, ea = lv.copy(), la.copy()
     for k in range(3):
         ev = ev + np.float32((sig[k + 1, 2] - sig[k, 2]) * 0.5)
