@@ -14,8 +14,16 @@ namespace h3 {
 
 namespace {
 
-constexpr int kMaxVec = 16;  // 8 bf16 per vector, so H <= 64 lanes * 16 * 8 = 8192
-
+// One wave per RW consecutive rows: each lane holds its NV 16-byte vectors
+// (columns 8c .. 8c+7, c = lane + 64 i) of every row in registers, so the
+// row is read once; the fp32 shift and scale of a column (64 bytes per 16
+// bytes of x) are read once for all RW rows, which share their segment except
+// where a segment ends inside the group (then a row reads its own).  Per
+// element the arithmetic is that of one row at a time: the lane's sum of
+// squares in column order, the wave sum, then the modulated value.  Two rows
+// per wave: 4 rows (half the occupancy) and the parameters staged in LDS per
+// workgroup (a 40 KB load before the first row) were both slower.
+template <int NV, int RW>
 __global__ __launch_bounds__(256) void k_modnorm(const bf16_t* __restrict__ x,
                                                  bf16_t* __restrict__ out, int out_row0,
                                                  const float* __restrict__ shift,
@@ -23,49 +31,74 @@ __global__ __launch_bounds__(256) void k_modnorm(const bf16_t* __restrict__ x,
                                                  int seg_stride, int row0, int row1, int H,
                                                  int n_text, int n_prefix, float eps) {
   const int lane = threadIdx.x & 63;
-  const int row = row0 + blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= row1) return;
+  const int rbase = row0 + (blockIdx.x * 4 + (threadIdx.x >> 6)) * RW;
+  if (rbase >= row1) return;
   const int nvec = H >> 3;
-  const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)row * H);
-  u32x4_t v[kMaxVec];
-  float ss = 0.f;
+  u32x4_t v[RW][NV];
+  float rinv[RW];
+  int sg[RW];
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nvec) {
-      v[i] = xr[c];
+  for (int r = 0; r < RW; ++r) {
+    const int row = rbase + r;
+    float ss = 0.f;
+    if (row < row1) {
+      const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)row * H);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float a = bflo(v[i][t]), b = bfhi(v[i][t]);
-        ss = fmaf(a, a, ss);
-        ss = fmaf(b, b, ss);
+      for (int i = 0; i < NV; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nvec) {
+          v[r][i] = xr[c];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float a = bflo(v[r][i][t]), b = bfhi(v[r][i][t]);
+            ss = fmaf(a, a, ss);
+            ss = fmaf(b, b, ss);
+          }
+        }
       }
     }
+    ss = wave_sum(ss);
+    rinv[r] = rsqrtf(ss / (float)H + eps);
+    sg[r] = row < n_text ? 0 : (row < n_prefix ? 1 : 2);
   }
-  ss = wave_sum(ss);
-  const float rinv = rsqrtf(ss / (float)H + eps);
-  const int sg = row < n_text ? 0 : (row < n_prefix ? 1 : 2);
-  const float* sh = shift + (size_t)sg * seg_stride;
-  const float* sc = scale + (size_t)sg * seg_stride;
-  u32x4_t* orow = reinterpret_cast<u32x4_t*>(out + (size_t)(row - out_row0) * H);
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c = lane + 64 * i;
-    if (c < nvec) {
-      const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sh + 8 * c);
-      const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(sh + 8 * c + 4);
-      const f32x4_t k0 = *reinterpret_cast<const f32x4_t*>(sc + 8 * c);
-      const f32x4_t k1 = *reinterpret_cast<const f32x4_t*>(sc + 8 * c + 4);
-      const float shv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      const float scv[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+    if (c >= nvec) continue;
+    float shv[8], scv[8];
+    auto params = [&](int seg) {
+      const float* sh = shift + (size_t)seg * seg_stride + 8 * c;
+      const float* sc = scale + (size_t)seg * seg_stride + 8 * c;
+      const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sh);
+      const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(sh + 4);
+      const f32x4_t k0 = *reinterpret_cast<const f32x4_t*>(sc);
+      const f32x4_t k1 = *reinterpret_cast<const f32x4_t*>(sc + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        shv[e] = s0[e];
+        shv[4 + e] = s1[e];
+        scv[e] = k0[e];
+        scv[4 + e] = k1[e];
+      }
+    };
+    params(sg[0]);
+    int cur = sg[0];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int row = rbase + r;
+      if (row >= row1) break;
+      if (sg[r] != cur) {  // a segment ends inside this wave's rows
+        params(sg[r]);
+        cur = sg[r];
+      }
       u32x4_t o;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float a = bflo(v[i][t]) * rinv, b = bfhi(v[i][t]) * rinv;
+        const float a = bflo(v[r][i][t]) * rinv[r], b = bfhi(v[r][i][t]) * rinv[r];
         o[t] = pack2(fmaf(a, 1.0f + scv[2 * t], shv[2 * t]),
                      fmaf(b, 1.0f + scv[2 * t + 1], shv[2 * t + 1]));
       }
-      orow[c] = o;
+      reinterpret_cast<u32x4_t*>(out + (size_t)(row - out_row0) * H)[c] = o;
     }
   }
 }
@@ -119,8 +152,18 @@ hipError_t launch_modnorm(const bf16_t* x, bf16_t* out, int out_row0, const floa
                           int n_text, int n_prefix, float eps, hipStream_t s) {
   const int n = row1 - row0;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_modnorm, dim3((n + 3) / 4), dim3(256), 0, s, x, out, out_row0, shift,
-                     scale, seg_stride, row0, row1, H, n_text, n_prefix, eps);
+  // vectors per lane: the row's H / 8 16-byte vectors over 64 lanes (H <= 8192)
+  const int nv = (H / 8 + 63) / 64;
+  auto go = [&](auto kern, int rw) {
+    const int waves = (n + rw - 1) / rw;
+    hipLaunchKernelGGL(kern, dim3((waves + 3) / 4), dim3(256), 0, s, x, out, out_row0, shift,
+                       scale, seg_stride, row0, row1, H, n_text, n_prefix, eps);
+  };
+  if (nv <= 2) go(k_modnorm<2, 2>, 2);
+  else if (nv <= 4) go(k_modnorm<4, 2>, 2);
+  else if (nv <= 8) go(k_modnorm<8, 2>, 2);
+  else if (nv <= 11) go(k_modnorm<11, 2>, 2);
+  else go(k_modnorm<16, 2>, 2);
   return hipGetLastError();
 }
 
