@@ -68,6 +68,9 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
 
   for (int c0 = 0; c0 < plen; c0 += 32) {
     // ---- q / k: row vector v = (it * 4 + wave) * RPW + slot; v < 32 is q ----
+    // A lane's k row in iteration it + NIT/2 is its q row of iteration it (v + 32),
+    // so the rotary cos/sin loaded for the q row serve the k row as well.
+    f32x4_t rope_cs[NIT / 2][4];
     u32x4_t raw[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -100,12 +103,15 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = x[e] * rinv * gg[e];
         if (a.rope) {
-          // cos/sin of pairs i = 8 (u mod LPR/2) + e of this row
-          const float* cs = a.rope + ((size_t)(r_beg + (real ? rl : 0)) * (D / 2) +
-                                      8 * (u % (LPR / 2))) * 2;
-          f32x4_t c4[4];
+          // cos/sin of pairs i = 8 (u mod LPR/2) + e of this row (loaded with the q row)
+          if (which == 0) {
+            const float* cs = a.rope + ((size_t)(r_beg + (real ? rl : 0)) * (D / 2) +
+                                        8 * (u % (LPR / 2))) * 2;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) c4[q4] = *reinterpret_cast<const f32x4_t*>(cs + 4 * q4);
+            for (int q4 = 0; q4 < 4; ++q4)
+              rope_cs[it % (NIT / 2)][q4] = *reinterpret_cast<const f32x4_t*>(cs + 4 * q4);
+          }
+          const f32x4_t* c4 = rope_cs[it % (NIT / 2)];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float c = c4[e >> 1][(e & 1) * 2], sn = c4[e >> 1][(e & 1) * 2 + 1];
