@@ -25,8 +25,12 @@
 // issues its half of stage s+1 at the start of its memory phase of stage s
 // (the buffer's last readers finished a phase earlier); group 1 issues its
 // half of stage s+2 at the end of its memory phase of stage s, right after its
-// own reads of that buffer.  Both thus have two phases to land their loads
-// before the barrier that precedes the first read.  The loads are issued as
+// own reads of that buffer.  The other waves of group 1 may still be reading
+// that buffer then, so group 1's half is made of rows no other wave of the
+// group reads: the A rows of group 0's sub-tiles (read a phase earlier) and,
+// per wave, half of the B rows that the wave itself reads.  Both groups thus
+// have two phases to land their loads before the barrier that precedes the
+// first read, and each phase carries half of the stage's loads.  The loads are issued as
 // inline assembly (scalar base address, per-lane 32-bit offsets) so that the
 // compiler does not insert its own conservative waits for them; this kernel
 // waits on vmcnt itself.
@@ -169,28 +173,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
   const int m0 = tm * BM, n0 = tn * BN;
   const int grp = wave >> 2, wm = wave >> 2, wn = wave & 3;
 
-  // Loads: a stage is 256 rows x 8 chunks per operand; thread t moves chunks
-  // 512 i + t (i < 4) of A and of B.  Byte offsets from the stage's column.
+  // Loads: a stage is 256 rows x 8 chunks per operand, moved in row groups of
+  // 8 rows (64 chunks, 1 KB of LDS: one load instruction of a wave, lane l
+  // taking chunk l).  Wave w of a group loads 4 row groups of each operand:
+  // group 1 those of A rows 0-127 (read only by group 0) and the first half
+  // of its own B rows, group 0 those of A rows 128-255 and the second half of
+  // the B rows of its SIMD partner (see the schedule).  Byte offsets from the
+  // stage's column.
   constexpr int ES = I8 ? 1 : 2;  // bytes per element
   const int rowb = K * ES;         // bytes per operand row
+  const int ra0 = 16 * (1 - grp) + 4 * wn, rb0 = 8 * wn + 4 * (1 - grp);  // first row groups
   uint32_t ga[4], gb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = i * 512 + tid;
-    const int r = q >> 3, gc = (q & 7) ^ swz(r);
+    const int c = lane & 7;
+    const int r = (ra0 + i) * 8 + (lane >> 3), rb = (rb0 + i) * 8 + (lane >> 3);
     // byte offsets below 2^32 (M K and N K are below 2^31); ragged M: clamp, rows >= M are dropped
-    ga[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)rowb + (uint32_t)(gc * 16);
-    gb[i] = (uint32_t)(n0 + r) * (uint32_t)rowb + (uint32_t)(gc * 16);
+    ga[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)rowb + (uint32_t)((c ^ swz(r)) * 16);
+    gb[i] = (uint32_t)(n0 + rb) * (uint32_t)rowb + (uint32_t)((c ^ swz(rb)) * 16);
   }
-  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 64 * 16);
+  const uint32_t lda = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + ra0 * 1024);
+  const uint32_t ldb =
+      (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + STAGE * 2 + rb0 * 1024);
   auto issue = [&](int s) {
     const void* pa = uniform_ptr(static_cast<const char*>(A) + s * STAGE_BYTES);
     const void* pb = uniform_ptr(static_cast<const char*>(B) + s * STAGE_BYTES);
-    const uint32_t l = lds0 + (uint32_t)((s & 1) * 2 * STAGE * 2);
+    const uint32_t so = (uint32_t)((s & 1) * 2 * STAGE * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dma16(pa, ga[i], l + i * 512 * 16);
-      dma16(pb, gb[i], l + STAGE * 2 + i * 512 * 16);
+      dma16(pa, ga[i], lda + so + i * 1024);
+      dma16(pb, gb[i], ldb + so + i * 1024);
     }
   };
 
@@ -439,29 +451,32 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8g(const int8_t* __restrict__ 
   const int m0 = tm * BMG, n0 = tn * BN;
   const int grp = wave >> 2, wm = wave >> 2, wn = wave & 3;
 
+  // row groups of 8 rows as in k_gemm_bf16: group 1 loads A rows 0-63 (read
+  // only by group 0) and the first half of its own B rows, group 0 the rest
   const uint32_t rowb = (uint32_t)K;
+  const int ra0 = 8 * (1 - grp) + 2 * wn, rb0 = 8 * wn + 4 * (1 - grp);
   uint32_t ga[2], gb[4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int q = i * 512 + tid;
-    const int r = q >> 3, gc = (q & 7) ^ swz(r);
-    ga[i] = (uint32_t)min(m0 + r, M - 1) * rowb + (uint32_t)(gc * 16);
+    const int r = (ra0 + i) * 8 + (lane >> 3);
+    ga[i] = (uint32_t)min(m0 + r, M - 1) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = i * 512 + tid;
-    const int r = q >> 3, gc = (q & 7) ^ swz(r);
-    gb[i] = (uint32_t)(n0 + r) * rowb + (uint32_t)(gc * 16);
+    const int r = (rb0 + i) * 8 + (lane >> 3);
+    gb[i] = (uint32_t)(n0 + r) * rowb + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
   }
-  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 64 * 16);
+  const uint32_t lda = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + ra0 * 1024);
+  const uint32_t ldb =
+      (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + SA * 2 + rb0 * 1024);
   auto issue = [&](int s) {
     const void* pa = uniform_ptr(A + s * STAGE_BYTES);
     const void* pb = uniform_ptr(B + s * STAGE_BYTES);
-    const uint32_t l = lds0 + (uint32_t)((s & 1) * SST * 2);
+    const uint32_t so = (uint32_t)((s & 1) * SST * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(pa, ga[i], l + i * 512 * 16);
+    for (int i = 0; i < 2; ++i) dma16(pa, ga[i], lda + so + i * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(pb, gb[i], l + SA * 2 + i * 512 * 16);
+    for (int i = 0; i < 4; ++i) dma16(pb, gb[i], ldb + so + i * 1024);
   };
 
   const int l16 = lane & 15, q4 = lane >> 4;

@@ -31,9 +31,11 @@ def _forward_inputs(sh, L, seed=42):
     return ts, npt, blocks, head, mods, mf, rope, x
 
 
-def _run_forward(sh, ts, npt, blocks, head, mods, mf, rope, x):
+def _run_forward(sh, ts, npt, blocks, head, mods, mf, rope, x, fill=None):
     shape = B.make_shape(sh, ts, npt)
     ws = T.workspace(B.workspace_bytes(shape, ts, B.H3_WS_DIT))
+    if fill is not None:  # byte pattern left in the workspace before the call
+        ws.fill_(fill)
     bd = [T.weights_to_dev(b) for b in blocks]
     hd = T.weights_to_dev(head)
     vv = torch.empty((sh.n_video, sh.c_video), dtype=torch.float32, device="cuda")
@@ -85,6 +87,26 @@ def test_forward_determinism():
     ha = hashlib.sha256(a[0].tobytes() + a[1].tobytes()).hexdigest()
     hb = hashlib.sha256(b[0].tobytes() + b[1].tobytes()).hexdigest()
     assert ha == hb
+
+
+# one row of tiles and K = 3072: every product of the block splits its K loop
+# and goes through the workspace's partial-sum slots
+WIDE = S.Shape(n_text=32, n_audio=32, n_video=192, hidden=3072, n_heads=24, head_dim=128,
+               ffn=3072, tile=64, top_k=2, pooled=1, mlp=1, gate=1)
+
+
+@pytest.mark.parametrize("name", ["tiny", "wide"])
+def test_forward_independent_of_workspace_contents(name):
+    """Every workspace byte a kernel reads was written earlier in the same call:
+    the velocities are the same bytes whatever the workspace held before."""
+    sh, L = (S.TINY, 2) if name == "tiny" else (WIDE, 1)
+    inp = _forward_inputs(sh, L)
+    hs = []
+    for fill in (0x00, 0x3C, 0xFF):
+        print(f"case: {name} forward, workspace bytes 0x{fill:02x}", flush=True)
+        v, a = _run_forward(sh, *inp, fill=fill)
+        hs.append(hashlib.sha256(v.tobytes() + a.tobytes()).hexdigest())
+    assert len(set(hs)) == 1, hs
 
 
 def test_full_size_block_sampled_rows():
