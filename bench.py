@@ -71,6 +71,10 @@ def parse():
                     help="only measure what the products and the row kernels can reach on this "
                          "GPU: an MFMA-only loop (h3_calibrate_mfma, bf16 16x16x32 on random "
                          "operands) and a 1 GiB device copy")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor bf16 GEMM (torch.mm, which runs hipBLASLt) on "
+                         "the default workload's four product shapes, as a reference point for "
+                         "the library's products (plain products: no bias or epilogue)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) three "
                          "times, to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -319,6 +323,37 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
+def vendor_gemm():
+    """torch.mm (hipBLASLt) on the QKV, out-projection, FC1 and FC2 shapes of
+    the default workload, C = A W^T with W stored [out][in] as the library's
+    weights are; median of 10 calls after 3 warm-ups, HIP events."""
+    import torch
+    from audio_diffusion_transformer_amd import synth as S
+    sh = S.FULL
+    R, H, F, A = sh.rows, sh.hidden, sh.ffn, sh.n_heads * sh.head_dim
+    torch.manual_seed(0)
+    for name, (M, N, K) in (("gemm_qkv", (R, 3 * A, H)), ("gemm_o", (R, H, A)),
+                            ("gemm_fc1", (R, F, H)), ("gemm_fc2", (R, H, F))):
+        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        w = torch.randn(N, K, device="cuda").to(torch.bfloat16)
+        for _ in range(3):
+            c = torch.mm(a, w.t())
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c = torch.mm(a, w.t())
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        print(json.dumps({"vendor_gemm": name, "M": M, "N": N, "K": K, "ms": round(ms, 4),
+                          "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}),
+              flush=True)
+        del a, w, c
+
+
 def kernel_work(sh, ts, npt, plan_sel_rows):
     """Algorithmic FLOP (GEMMs, attention) and bytes (norm) per launch."""
     R, H, F, nh, d = sh.rows, sh.hidden, sh.ffn, sh.n_heads, sh.head_dim
@@ -398,6 +433,9 @@ def main():
         return
     if args.calibrate:
         calibrate()
+        return
+    if args.vendor_gemm:
+        vendor_gemm()
         return
     if args.attn_sweep:
         attn_sweep()
