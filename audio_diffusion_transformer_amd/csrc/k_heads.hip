@@ -66,12 +66,13 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
   };
   const float inv_d = 1.0f / (float)D;
 
-  for (int c0 = 0; c0 < plen; c0 += 32) {
-    // ---- q / k: row vector v = (it * 4 + wave) * RPW + slot; v < 32 is q ----
-    // A lane's k row in iteration it + NIT/2 is its q row of iteration it (v + 32),
-    // so the rotary cos/sin loaded for the q row serve the k row as well.
-    f32x4_t rope_cs[NIT / 2][4];
-    u32x4_t raw[NIT];
+  // The q / k row vectors (vector v = (it * 4 + wave) * RPW + slot, v < 32 is
+  // q) and the v rows of the group of 32 rows at c0.  The next group's are
+  // loaded before this group's v sums and transpose, so that their latency
+  // passes under them.
+  constexpr int NVL = 32 * LPR / 256;  // 16-byte units of the group's v rows per thread
+  u32x4_t raw[NIT], vraw[NVL];
+  auto load_rows = [&](int c0) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int v = (it * 4 + wave) * RPW + slot;
@@ -79,6 +80,29 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
       raw[it] = (u32x4_t){0u, 0u, 0u, 0u};
       if (rl < len) raw[it] = *reinterpret_cast<const u32x4_t*>(src_of(v >> 5, r_beg + rl));
     }
+    // v: unit k2 * 256 + tid is row unit / LPR, 16-byte unit unit % LPR
+#pragma unroll
+    for (int k2 = 0; k2 < NVL; ++k2) {
+      const int unit = k2 * 256 + tid;
+      const int rl = c0 + unit / LPR, uu = unit % LPR;
+      vraw[k2] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (rl < len) {
+        if constexpr (MODE == HEADS_QKV)
+          vraw[k2] = *reinterpret_cast<const u32x4_t*>(a.y + (size_t)(r_beg + rl) * a.ystride +
+                                                        h * a.parts * D + 2 * D + 8 * uu);
+        else
+          vraw[k2] = *reinterpret_cast<const u32x4_t*>(
+              a.v_in + ((size_t)h * a.R + r_beg + rl) * D + 8 * uu);
+      }
+    }
+  };
+  load_rows(0);
+
+  for (int c0 = 0; c0 < plen; c0 += 32) {
+    // ---- q / k ----
+    // A lane's k row in iteration it + NIT/2 is its q row of iteration it (v + 32),
+    // so the rotary cos/sin loaded for the q row serve the k row as well.
+    f32x4_t rope_cs[NIT / 2][4];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int v = (it * 4 + wave) * RPW + slot;
@@ -135,21 +159,11 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
     }
     // ---- v: 32 rows x LPR units, staged row-major in LDS ----
 #pragma unroll
-    for (int k2 = 0; k2 < 32 * LPR / 256; ++k2) {
+    for (int k2 = 0; k2 < NVL; ++k2) {
       const int unit = k2 * 256 + tid;
-      const int r = unit / LPR, uu = unit % LPR;
-      const int rl = c0 + r;
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (rl < len) {
-        if constexpr (MODE == HEADS_QKV)
-          w = *reinterpret_cast<const u32x4_t*>(a.y + (size_t)(r_beg + rl) * a.ystride +
-                                                 h * a.parts * D + 2 * D + 8 * uu);
-        else
-          w = *reinterpret_cast<const u32x4_t*>(a.v_in + ((size_t)h * a.R + r_beg + rl) * D +
-                                                 8 * uu);
-      }
-      *reinterpret_cast<u32x4_t*>(&sV[r * SV + 8 * uu]) = w;
+      *reinterpret_cast<u32x4_t*>(&sV[(unit / LPR) * SV + 8 * (unit % LPR)]) = vraw[k2];
     }
+    if (c0 + 32 < plen) load_rows(c0 + 32);
     __syncthreads();
     // v sums: this lane's columns 8u..8u+7 over rows slot, slot + RPW, ... of the
     // wave's share (rows wave * 8 .. wave * 8 + 7)
