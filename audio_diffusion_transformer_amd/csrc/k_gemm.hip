@@ -380,6 +380,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
     }
     return;
   }
+  // Gated residual: this lane's residual chunks (the output chunks it writes
+  // below) are loaded before the staging, so that their latency passes under it.
+  u32x4_t xres[2 * NI];
+  if constexpr (EPI == EPI_BIAS_RESGATE) {
+#pragma unroll
+    for (int t = 0; t < 2 * NI; ++t) {
+      const int q = (t + 2 * ib) * 64 + lane;
+      const int row = m0 + wm * 128 + (q >> 3);
+      xres[t] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (row < M)
+        xres[t] = *reinterpret_cast<const u32x4_t*>(ep.res + (size_t)row * N + n0 + wn * 64 +
+                                                    (q & 7) * 8);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float bias = bf2f(ep.bias[n0 + wn * 64 + j * 16 + l16]);
@@ -395,7 +409,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
+#pragma unroll
   for (int t = 0; t < 2 * NI; ++t) {  // 8 rows per t
     const int q = (t + 2 * ib) * 64 + lane;
     const int r = q >> 3, c8 = (q & 7) * 8;
@@ -405,7 +419,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + r * 64 + c8);
     const size_t o = (size_t)row * N + col;
     if constexpr (EPI == EPI_BIAS_RESGATE) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ep.res + o);
+      const u32x4_t x = xres[t];
       const float* gp =
           ep.gate + (size_t)seg_of(row, ep.n_text, ep.n_prefix) * ep.gate_seg_stride + col;
       const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
