@@ -92,12 +92,12 @@ TRAFFIC = {
     "sources": ["audio_diffusion_transformer_amd/csrc/k_gemm.hip",
                 "audio_diffusion_transformer_amd/csrc/common.h",
                 "audio_diffusion_transformer_amd/csrc/internal.h"],
-    "sources_sha256": "be549c37b65fec19f2d45e72aa7d9e4a2035b1519fc0b01c122d5f3cb7cd1887",
+    "sources_sha256": "a3fe8142b901224c92fa2b95fd93314923a57a2b5dff40c0542a91f6550babe7",
     # raw KiB of one FC1 call, its two launches summed (the tiles with the
-    # split last round: 2339047.6666666665 + 32817.5 fetched, 681250.0 + 1686.0 written),
+    # split last round: 2341368.3125 + 32817.5 fetched, 681250.0 + 1686.0 written),
     # and the copy's scale factors (1 GiB copy: FETCH_SIZE 524294.5 KiB,
     # WRITE_SIZE 1048576.0 KiB)
-    "fetch_kib": 2371865.1666666665, "fetch_scale": 1.999975,
+    "fetch_kib": 2374185.8125, "fetch_scale": 1.999975,
     "write_kib": 682936.0, "write_scale": 1.000000,
 }
 
