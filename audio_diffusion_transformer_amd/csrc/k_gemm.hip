@@ -586,6 +586,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8g(const int8_t* __restrict__ 
   __syncthreads();
 
   // ---- epilogue: bias, bf16, gated residual (as EPI_BIAS_RESGATE) ----
+  // the residual chunks this lane writes, loaded before the staging
+  u32x4_t xres[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int q = t * 64 + lane;
+    const int row = m0 + wm * 64 + (q >> 3);
+    xres[t] = (u32x4_t){0u, 0u, 0u, 0u};
+    if (row < M)
+      xres[t] = *reinterpret_cast<const u32x4_t*>(ep.res + (size_t)row * N + n0 + wn * 64 +
+                                                  (q & 7) * 8);
+  }
   bf16_t* st = smem + wave * (64 * 64);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8g(const int8_t* __restrict__ 
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
+#pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int q = t * 64 + lane;
     const int r = q >> 3, c8 = (q & 7) * 8;
@@ -610,7 +621,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8g(const int8_t* __restrict__ 
     const int col = n0 + wn * 64 + c8;
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + r * 64 + c8);
     const size_t o = (size_t)row * N + col;
-    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ep.res + o);
+    const u32x4_t x = xres[t];
     const float* gp =
         ep.gate + (size_t)seg_of(row, ep.n_text, ep.n_prefix) * ep.gate_seg_stride + col;
     const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
