@@ -17,8 +17,10 @@
 // so the larger key is the larger score and, between equal scores, the lower
 // tile; keys are distinct.  The k-th largest key T is found bit by bit from
 // the top (a candidate bit stays set when at least k keys are >= the
-// candidate, counted with wave ballots), and the selected tiles are exactly
-// the keys >= T, written in ascending tile order from the ballot masks.
+// candidate, counted with wave ballots; the low word's bits above the tile
+// ids, set in every real key, are set without counting), and the selected
+// tiles are exactly the keys >= T, written in ascending tile order from the
+// ballot masks.
 #include "common.h"
 #include "internal.h"
 
@@ -52,30 +54,46 @@ __global__ __launch_bounds__(64 * kQT) void k_route(RouteArgs a) {
   if (active)
     for (int c = lane; c < D; c += 64) sQ[wave][c] = a.qbar[((size_t)h * nQ + i) * D + c];
 
-  // rows j0 .. j0+63 (those < nT) of a [nT][D] table into sRow
-  auto stage = [&](const float* src, int j0) {
+  // Rows j0 .. j0+63 of a [nT][D] table (rows >= nT as zeros) pass through
+  // registers into sRow: the next group's loads are issued before the current
+  // group is used, so their latency passes under the work on it.
+  constexpr int NSL = 64 * (D / 4) / (64 * kQT);  // 16-byte units per thread and group
+  f32x4_t sreg[NSL];
+  auto load_stage = [&](const float* src, int j0) {
     const int rows = min(64, nT - j0);
-    for (int idx = tid; idx < 64 * (D / 4); idx += 64 * kQT) {
+#pragma unroll
+    for (int k = 0; k < NSL; ++k) {
+      const int idx = k * 64 * kQT + tid;
       const int r = idx / (D / 4), c4 = idx % (D / 4);
-      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-      if (r < rows) v = *reinterpret_cast<const f32x4_t*>(src + (size_t)(j0 + r) * D + 4 * c4);
-      *reinterpret_cast<f32x4_t*>(&sRow[r * SR + 4 * c4]) = v;
+      sreg[k] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      if (r < rows) sreg[k] = *reinterpret_cast<const f32x4_t*>(src + (size_t)(j0 + r) * D + 4 * c4);
+    }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int k = 0; k < NSL; ++k) {
+      const int idx = k * 64 * kQT + tid;
+      *reinterpret_cast<f32x4_t*>(&sRow[(idx / (D / 4)) * SR + 4 * (idx % (D / 4))]) = sreg[k];
     }
   };
 
   // ---- scores: lane l scores tile 64 t + l ----
   const float scale = rsqrtf((float)D);
   const float* kb = a.kbar + (size_t)h * nT * D;
+  const float* vb = a.vbar + (size_t)h * nT * D;
   float* srow_out = a.scores + ((size_t)h * nQ + i) * nT;
   float sc[PL];
   bool any_nan = false;
+  load_stage(kb, 0);
 #pragma unroll
   for (int t = 0; t < PL; ++t) {
     sc[t] = 0.f;
     if (t < ntl) {
       __syncthreads();
-      stage(kb, 64 * t);
+      store_stage();
       __syncthreads();
+      if (t + 1 < ntl) load_stage(kb, 64 * (t + 1));
+      else if (a.use_pooled) load_stage(vb, 0);  // first v-bar rows, under the top-k
       const int j = 64 * t + lane;
       if (active && j < nT) {
         const float* kr = &sRow[lane * SR];
@@ -111,8 +129,18 @@ __global__ __launch_bounds__(64 * kQT) void k_route(RouteArgs a) {
                      ? (((uint64_t)order_key(sc[t]) << 32) | (uint32_t)(~j))
                      : 0ull;  // below every real key
       }
-      uint64_t T = 0;  // the top_k-th largest key, built from the top bit down
+      // T, the top_k-th largest key, built from the top bit down.  It is a
+      // real key (top_k < nQ real keys), and every real key's low word ~j has
+      // all bits from log2(nT) up set (j < nT): those bits of T are set
+      // without counting.
+      int idb = 0;  // bits of a tile id
+      while ((1 << idb) < nT) ++idb;
+      uint64_t T = 0;
       for (int b = 63; b >= 0; --b) {
+        if (b < 32 && b >= idb) {
+          T |= 1ull << b;
+          continue;
+        }
         const uint64_t cand = T | (1ull << b);
         int cnt = 0;
 #pragma unroll
@@ -149,7 +177,6 @@ __global__ __launch_bounds__(64 * kQT) void k_route(RouteArgs a) {
     l += sc[t];
   }
   l = wave_sum(l);
-  const float* vb = a.vbar + (size_t)h * nT * D;
   float acc[D / 64];
 #pragma unroll
   for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
@@ -157,8 +184,9 @@ __global__ __launch_bounds__(64 * kQT) void k_route(RouteArgs a) {
   for (int t = 0; t < PL; ++t) {
     if (t < ntl) {
       __syncthreads();
-      stage(vb, 64 * t);
+      store_stage();
       __syncthreads();
+      if (t + 1 < ntl) load_stage(vb, 64 * (t + 1));
       // rows past nT are staged as zeros and their weights are 0: adding
       // 0 * 0 leaves the sum unchanged, so all 64 rows run unconditionally
 #pragma unroll 16
