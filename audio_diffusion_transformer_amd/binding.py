@@ -173,6 +173,103 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# Host-side checks of the tensors handed to the library.  The C ABI receives
+# bare device pointers and cannot see a buffer's size, so a tensor of the wrong
+# size, type or device would turn into an out-of-bounds device access; these
+# checks refuse it with H3_EINVAL before any call.
+_KINDS = {"bf16": ("int16", "uint16", "bfloat16"), "f32": ("float32",), "i32": ("int32",),
+          "i8": ("int8",), "u8": ("uint8",)}
+
+
+class _Checks:
+    """Type, size and layout of each tensor are checked as it is named; the
+    device of all of them at the end (done), so a wrong size is reported even
+    for host tensors."""
+
+    def __init__(self):
+        self.named = []
+
+    def __call__(self, t, name, numel, kind, optional=False):
+        if t is None:
+            if optional:
+                return
+            raise H3Error(H3_EINVAL, f"{name}: a tensor is required")
+        dt = str(t.dtype).replace("torch.", "")
+        if dt not in _KINDS[kind]:
+            raise H3Error(H3_EINVAL, f"{name}: dtype {dt}, expected {kind}")
+        if numel is not None and t.numel() != numel:
+            raise H3Error(H3_EINVAL, f"{name}: {t.numel()} elements, expected {numel}")
+        if not t.is_contiguous():
+            raise H3Error(H3_EINVAL, f"{name}: not contiguous")
+        self.named.append((name, t))
+
+    def done(self):
+        for name, t in self.named:
+            if not t.is_cuda:
+                raise H3Error(H3_EINVAL, f"{name}: not a device tensor")
+
+
+class _Dims:
+    """Tensor sizes implied by an H3Shape (see include/h3.h)."""
+
+    def __init__(self, s: H3Shape):
+        self.T, self.A_rows, self.V = s.n_text, s.n_audio, s.n_video
+        self.R = s.n_text + s.n_audio + s.n_video
+        self.H, self.nh, self.d, self.F = s.hidden, s.n_heads, s.head_dim, s.ffn
+        self.A = s.n_heads * s.head_dim
+        self.parts = 3 + (1 if s.gate else 0)
+        self.F1 = 2 * s.ffn if s.mlp == 1 else s.ffn
+        self.nT, self.npt = s.n_tiles, s.n_prefix_tiles
+        self.nQ = s.n_tiles - s.n_prefix_tiles
+        self.nsel = min(s.top_k, self.nQ) if self.nQ > 0 else 0
+
+
+def _check_block_weights(_expect, w, D: _Dims, tag=""):
+    if not isinstance(w, dict):
+        return  # a prebuilt struct: the caller vouches for its pointers
+    for n, numel in (("w_qkv", D.parts * D.A * D.H), ("b_qkv", D.parts * D.A),
+                     ("q_gain", D.d), ("k_gain", D.d), ("w_o", D.H * D.A), ("b_o", D.H),
+                     ("w_fc1", D.F1 * D.H), ("b_fc1", D.F1), ("w_fc2", D.H * D.F),
+                     ("b_fc2", D.H)):
+        _expect(w.get(n), tag + n, numel, "bf16")
+
+
+def _check_block_weights_i8(_expect, w, D: _Dims, tag=""):
+    if not isinstance(w, dict):
+        return
+    for n, rows, cols in (("qkv", D.parts * D.A, D.H), ("o", D.H, D.A), ("fc1", D.F1, D.H),
+                          ("fc2", D.H, D.F)):
+        _expect(w.get("w_" + n), tag + "w_" + n, rows * cols, "i8")
+        _expect(w.get("s_" + n), tag + "s_" + n, rows, "f32")
+        _expect(w.get("b_" + n), tag + "b_" + n, rows, "bf16")
+    _expect(w.get("q_gain"), tag + "q_gain", D.d, "bf16")
+    _expect(w.get("k_gain"), tag + "k_gain", D.d, "bf16")
+
+
+def _check_heads(_expect, hw, D: _Dims):
+    if not isinstance(hw, dict):
+        return
+    cv, ca = int(hw["w_video"].shape[0]), int(hw["w_audio"].shape[0])
+    _expect(hw["w_video"], "w_video", cv * D.H, "bf16")
+    _expect(hw.get("b_video"), "b_video", cv, "bf16")
+    _expect(hw["w_audio"], "w_audio", ca * D.H, "bf16")
+    _expect(hw.get("b_audio"), "b_audio", ca, "bf16")
+    return cv, ca
+
+
+def _check_forward_io(_expect, D: _Dims, n_blocks, heads, mod, mod_final, rope, x_in, vel_video,
+                      vel_audio, ws):
+    _expect(mod, "mod", n_blocks * 3 * 6 * D.H, "f32")
+    _expect(mod_final, "mod_final", 3 * 2 * D.H, "f32")
+    _expect(rope, "rope", D.R * D.d, "f32", optional=True)
+    _expect(x_in, "x_in", D.R * D.H, "bf16")
+    c = _check_heads(_expect, heads, D)
+    if c is not None:
+        _expect(vel_video, "vel_video", D.V * c[0], "f32")
+        _expect(vel_audio, "vel_audio", D.A_rows * c[1], "f32")
+    _expect(ws, "ws", None, "u8")
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -207,6 +304,14 @@ def head_weights_struct(hw):
 
 
 def block_forward(shape, tile_start, w, mod, rope, x_in, x_out, ws, stream=None):
+    D, _expect = _Dims(shape), _Checks()
+    _check_block_weights(_expect, w, D)
+    _expect(mod, "mod", 3 * 6 * D.H, "f32")
+    _expect(rope, "rope", D.R * D.d, "f32", optional=True)
+    _expect(x_in, "x_in", D.R * D.H, "bf16")
+    _expect(x_out, "x_out", D.R * D.H, "bf16")
+    _expect(ws, "ws", None, "u8")
+    _expect.done()
     ts, tp = _tiles(tile_start)
     ws_struct = block_weights_struct(w) if isinstance(w, dict) else w
     _check(lib().h3_block_forward(ctypes.byref(shape), tp, ctypes.byref(ws_struct), _ptr(mod),
@@ -217,6 +322,12 @@ def block_forward(shape, tile_start, w, mod, rope, x_in, x_out, ws, stream=None)
 def dit_forward(shape, tile_start, blocks, heads, mod, mod_final, rope, x_in, vel_video,
                 vel_audio, ws, stream=None):
     """blocks: list of weight dicts or a prebuilt (H3BlockWeights * L) array."""
+    D, _expect = _Dims(shape), _Checks()
+    for l, b in enumerate(blocks if isinstance(blocks, (list, tuple)) else ()):
+        _check_block_weights(_expect, b, D, f"block {l} ")
+    _check_forward_io(_expect, D, len(blocks), heads, mod, mod_final, rope, x_in, vel_video,
+                      vel_audio, ws)
+    _expect.done()
     ts, tp = _tiles(tile_start)
     if isinstance(blocks, (list, tuple)):
         arr = (H3BlockWeights * max(len(blocks), 1))(*[block_weights_struct(b) for b in blocks])
@@ -232,6 +343,15 @@ def dit_forward(shape, tile_start, blocks, heads, mod, mod_final, rope, x_in, ve
 
 def routed_attn(shape, tile_start, q, k, v, out, ws, sel=None, scores=None, gate=None,
                 stream=None):
+    D, _expect = _Dims(shape), _Checks()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _expect(t, n, D.nh * D.R * D.d, "bf16")
+    _expect(gate, "gate", D.R * D.A, "bf16", optional=True)
+    _expect(out, "out", D.R * D.A, "bf16")
+    _expect(sel, "sel", D.nh * D.nQ * D.nsel, "i32", optional=True)
+    _expect(scores, "scores", D.nh * D.nQ * D.nT, "f32", optional=True)
+    _expect(ws, "ws", None, "u8")
+    _expect.done()
     ts, tp = _tiles(tile_start)
     _check(lib().h3_routed_attn(ctypes.byref(shape), tp, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                                 _ptr(out), _ptr(sel), _ptr(scores), _ptr(ws),
@@ -254,10 +374,39 @@ def _f32_host(a):
     return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
 
 
+def _check_rows_in(_expect, D: _Dims, w, text_rows):
+    if not isinstance(w, dict):
+        return None
+    cv, ca = int(w["w_video"].shape[1]), int(w["w_audio"].shape[1])
+    _expect(w["w_video"], "w_video", D.H * cv, "f32")
+    _expect(w.get("b_video"), "b_video", D.H, "f32")
+    _expect(w["w_audio"], "w_audio", D.H * ca, "f32")
+    _expect(w.get("b_audio"), "b_audio", D.H, "f32")
+    _expect(text_rows, "text_rows", D.T * D.H, "bf16")
+    return cv, ca
+
+
 def rows_in(shape, w, text_rows, audio_patch, video_patch, x, stream=None):
+    D, _expect = _Dims(shape), _Checks()
+    c = _check_rows_in(_expect, D, w, text_rows)
+    if c is not None:
+        _expect(audio_patch, "audio_patch", D.A_rows * c[1], "f32")
+        _expect(video_patch, "video_patch", D.V * c[0], "f32")
+    _expect(x, "x", D.R * D.H, "bf16")
+    _expect.done()
     ws_ = rows_in_weights_struct(w) if isinstance(w, dict) else w
     _check(lib().h3_rows_in(ctypes.byref(shape), ctypes.byref(ws_), _ptr(text_rows),
                             _ptr(audio_patch), _ptr(video_patch), _ptr(x), _stream(stream)))
+
+
+def _check_time_weights(_expect, tw, D: _Dims, n_blocks):
+    if not isinstance(tw, dict):
+        return
+    H = D.H
+    for n, numel in (("w1", H * 256), ("b1", H), ("w2", H * H), ("b2", H), ("w_mod", 6 * H * H),
+                     ("b_mod", 6 * H), ("mod_table", n_blocks * 6 * H), ("w_final", 2 * H * H),
+                     ("b_final", 2 * H)):
+        _expect(tw.get(n), n, numel, "bf16")
 
 
 def modulation_workspace_bytes(shape):
@@ -269,6 +418,12 @@ def modulation_workspace_bytes(shape):
 
 def modulation(shape, n_blocks, tw, sigma3, mod, mod_final, ws, stream=None):
     """sigma3: host (text, audio, video) timesteps."""
+    D, _expect = _Dims(shape), _Checks()
+    _check_time_weights(_expect, tw, D, n_blocks)
+    _expect(mod, "mod", n_blocks * 3 * 6 * D.H, "f32")
+    _expect(mod_final, "mod_final", 3 * 2 * D.H, "f32")
+    _expect(ws, "ws", None, "u8")
+    _expect.done()
     tws = time_weights_struct(tw) if isinstance(tw, dict) else tw
     sg, sp = _f32_host(sigma3)
     _check(lib().h3_modulation(ctypes.byref(shape), n_blocks, ctypes.byref(tws), sp, _ptr(mod),
@@ -287,6 +442,21 @@ def denoise_workspace_bytes(shape, tile_start, n_blocks):
 def denoise(shape, tile_start, blocks, heads, rows_w, tw, sigmas, rope, text_rows, video_latent,
             audio_latent, ws, stream=None):
     """sigmas: host [n_steps + 1][3]; the latents (fp32 device) are updated in place."""
+    D, _expect = _Dims(shape), _Checks()
+    for l, b in enumerate(blocks if isinstance(blocks, (list, tuple)) else ()):
+        _check_block_weights(_expect, b, D, f"block {l} ")
+    _check_time_weights(_expect, tw, D, len(blocks))
+    ch = _check_heads(_expect, heads, D)
+    ci = _check_rows_in(_expect, D, rows_w, text_rows)
+    if ch is not None and ci is not None and ch != ci:
+        raise H3Error(H3_EINVAL, f"head widths {ch} differ from the patch widths {ci}")
+    c = ch or ci
+    if c is not None:
+        _expect(video_latent, "video_latent", D.V * c[0], "f32")
+        _expect(audio_latent, "audio_latent", D.A_rows * c[1], "f32")
+    _expect(rope, "rope", D.R * D.d, "f32", optional=True)
+    _expect(ws, "ws", None, "u8")
+    _expect.done()
     ts, tp = _tiles(tile_start)
     if isinstance(blocks, (list, tuple)):
         arr = (H3BlockWeights * max(len(blocks), 1))(*[block_weights_struct(b) for b in blocks])
@@ -324,6 +494,15 @@ def dit_forward_tr_workspace_bytes(shape, tile_start, tr: TokenReduction):
 
 def dit_forward_tr(shape, tile_start, tr: TokenReduction, blocks, heads, mod, mod_final, rope,
                    x_in, vel_video, vel_audio, ws, stream=None):
+    D, _expect = _Dims(shape), _Checks()
+    for l, b in enumerate(blocks if isinstance(blocks, (list, tuple)) else ()):
+        _check_block_weights(_expect, b, D, f"block {l} ")
+    _check_forward_io(_expect, D, len(blocks), heads, mod, mod_final, rope, x_in, vel_video,
+                      vel_audio, ws)
+    Dr = _Dims(tr.shape)
+    _expect(tr.pairs, "pairs", Dr.V * 2, "i32")
+    _expect(tr.rope, "reduced rope", Dr.R * Dr.d, "f32", optional=True)
+    _expect.done()
     ts, tp = _tiles(tile_start)
     if isinstance(blocks, (list, tuple)):
         arr = (H3BlockWeights * max(len(blocks), 1))(*[block_weights_struct(b) for b in blocks])
@@ -340,6 +519,11 @@ def dit_forward_tr(shape, tile_start, tr: TokenReduction, blocks, heads, mod, mo
 def quantize_rows(x, q, scale, group=0, stream=None):
     """int8 codes of the bf16 matrix x [rows][cols] (device tensors)."""
     rows, cols = x.shape
+    _expect = _Checks()
+    _expect(x, "x", rows * cols, "bf16")
+    _expect(q, "q", rows * cols, "i8")
+    _expect(scale, "scale", rows * (cols // group if group > 0 else 1), "f32")
+    _expect.done()
     _check(lib().h3_quantize_rows(_ptr(x), rows, cols, group, _ptr(q), _ptr(scale),
                                   _stream(stream)))
 
@@ -365,6 +549,12 @@ def dit_forward_i8(shape, tile_start, blocks, heads, mod, mod_final, rope, x_in,
                    vel_audio, ws, fc2_group=1024, stream=None):
     """blocks: list of int8 weight dicts (quantize_block) or a prebuilt array.
     fc2_group: 1024 (the FC2 input per 1,024 channels) or 0 (per row)."""
+    D, _expect = _Dims(shape), _Checks()
+    for l, b in enumerate(blocks if isinstance(blocks, (list, tuple)) else ()):
+        _check_block_weights_i8(_expect, b, D, f"block {l} ")
+    _check_forward_io(_expect, D, len(blocks), heads, mod, mod_final, rope, x_in, vel_video,
+                      vel_audio, ws)
+    _expect.done()
     ts, tp = _tiles(tile_start)
     if isinstance(blocks, (list, tuple)):
         arr = (H3BlockWeightsI8 * max(len(blocks), 1))(*[block_weights_i8_struct(b) for b in blocks])
@@ -382,6 +572,12 @@ def calibrate_mfma(operands, n_blocks, iters, sink, stream=None):
     """Matrix-core calibration (h3_calibrate_mfma): operands a device tensor of
     random bf16 data, sink a device tensor of >= 256 floats.  Returns the FLOP
     the call performs; the caller times it."""
+    _expect = _Checks()
+    _expect(operands, "operands", None, "bf16")
+    _expect(sink, "sink", None, "f32")
+    if sink.numel() < 256:
+        raise H3Error(H3_EINVAL, "sink: fewer than 256 floats")
+    _expect.done()
     _check(lib().h3_calibrate_mfma(_ptr(operands), operands.numel() * operands.element_size(),
                                    n_blocks, iters, _ptr(sink), _stream(stream)))
     return n_blocks * 4 * iters * 16 * 16384

@@ -24,7 +24,6 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     # keep the compiler from forming packed fp32 VALU ops in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics",
 ]
 
 

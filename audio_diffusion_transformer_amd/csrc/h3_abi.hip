@@ -105,6 +105,13 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
     if (p.tstart[t + 1] <= p.tstart[t]) return fail(H3_EINVAL, "tile map not increasing at %d", t);
   if (p.tstart[p.npt] != p.P)
     return fail(H3_EINVAL, "prefix tiles end at row %d, prefix has %d rows", p.tstart[p.npt], p.P);
+  {
+    // the text/audio boundary must be a tile edge too: a tile holding rows of
+    // both segments would mix them in its means
+    bool edge = false;
+    for (int t = 0; t <= p.npt; ++t) edge = edge || p.tstart[t] == s->n_text;
+    if (!edge) return fail(H3_EINVAL, "no tile edge at the text/audio boundary (row %d)", s->n_text);
+  }
   p.nQ = p.nT - p.npt;
   if (p.nQ > 0 && s->top_k < 1) return fail(H3_EINVAL, "top_k must be >= 1");
   p.nsel = p.nQ > 0 ? (s->top_k < p.nQ ? s->top_k : p.nQ) : 0;

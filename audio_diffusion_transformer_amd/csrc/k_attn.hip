@@ -80,11 +80,14 @@ __device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
 }
 
 // 16 bytes per lane from (sbase + voff) into LDS at (m0 + 16 * lane): sbase a
-// wave-uniform address in SGPRs, voff a per-lane byte offset.  The compiler
-// does not track this load; the kernel waits for it on vmcnt itself.
+// wave-uniform address in SGPRs, voff a per-lane byte offset, with the one
+// wait state the ISA asks for between the M0 write and the load.  M0 is a
+// reserved register the compiler allocates no value to (a build test checks
+// that the kernels' assembly writes it only here).  The compiler does not
+// track this load; the kernel waits for it on vmcnt itself.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(lds)
                : "memory");
 }
 

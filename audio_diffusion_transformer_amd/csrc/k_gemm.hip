@@ -74,13 +74,14 @@ __device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
 }
 
 // 16 bytes per lane from (sbase + voff) into LDS at (m0 + 16 * lane): sbase a
-// wave-uniform address in SGPRs, voff a per-lane byte offset.  M0 is a
-// reserved register that the compiler does not allocate (gfx9+ LDS
-// instructions do not read it), so setting it here disturbs no
-// compiler-managed value.
+// wave-uniform address in SGPRs, voff a per-lane byte offset.  The ISA asks
+// for one wait state between a write of M0 and a global load into LDS that
+// reads it (the s_nop).  M0 is a reserved register: the compiler rejects it as
+// a clobber and allocates no value to it; a build test checks that the
+// kernels' assembly writes M0 only here and reads it only in these loads.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(lds)
                : "memory");
 }
 

@@ -129,6 +129,8 @@ def check_tile_map(tile_start, n_text, n_audio, n_video, n_prefix_tiles):
     R = n_text + n_audio + n_video
     assert ts[0] == 0 and ts[-1] == R and np.all(np.diff(ts) > 0)
     assert ts[n_prefix_tiles] == n_text + n_audio
+    # every segment boundary is a tile edge: text | audio as well as prefix | video
+    assert n_text in ts[:n_prefix_tiles + 1]
     return ts
 
 

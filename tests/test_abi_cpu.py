@@ -113,6 +113,7 @@ def test_workspace_layout_is_consistent(lib):
     (lambda s, t: setattr(s, "ffn", 1000), B.H3_EUNSUPPORTED),
     (lambda s, t: setattr(s, "n_prefix_tiles", 1), B.H3_EINVAL),
     (lambda s, t: t.__setitem__(3, t[2]), B.H3_EINVAL),
+    (lambda s, t: t.__setitem__(1, 32), B.H3_EINVAL),   # tile [32, 128) straddles text | audio
     (lambda s, t: t.__setitem__(-1, t[-1] + 1), B.H3_EINVAL),
     (lambda s, t: setattr(s, "top_k", 0), B.H3_EINVAL),
     (lambda s, t: setattr(s, "n_text", -1), B.H3_EINVAL),
@@ -274,3 +275,45 @@ def test_size_limits_on_host(lib, n_video, top_k, hidden, code):
                                  B.H3_WS_BLOCK, ctypes.byref(lay))
     assert rc == code, B.last_error()
 
+
+
+def test_binding_refuses_wrong_tensors_before_any_call():
+    """The binding checks every tensor's type, element count, layout and device
+    against the shape on the host (the C ABI cannot see buffer sizes), so a
+    wrong tensor raises H3Error instead of reaching a kernel."""
+    import torch
+    sh = S.TINY
+    shape, ts = _shape(sh)
+    R, H, nh, d = sh.rows, sh.hidden, sh.n_heads, sh.head_dim
+    bf = lambda n: torch.zeros(n, dtype=torch.int16)
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+    w = {k: bf(int(np.prod(v))) for k, v in S.block_shapes(sh).items()}
+    ws = torch.zeros(256, dtype=torch.uint8)
+    mod, rope, x, xo = f32(18 * H), f32(R * d), bf(R * H), bf(R * H)
+
+    def refused(fn, what):
+        with pytest.raises(B.H3Error) as e:
+            fn()
+        assert e.value.code == B.H3_EINVAL and what in str(e.value), str(e.value)
+
+    # right sizes on the host: refused only because they are not device tensors
+    refused(lambda: B.block_forward(shape, ts, w, mod, rope, x, xo, ws), "not a device tensor")
+    # wrong element counts, types and layouts are named
+    refused(lambda: B.block_forward(shape, ts, w, f32(17 * H), rope, x, xo, ws), "mod: ")
+    refused(lambda: B.block_forward(shape, ts, w, mod, f32(R * d - 2), x, xo, ws), "rope: ")
+    refused(lambda: B.block_forward(shape, ts, w, mod, rope, bf(R * H - 1), xo, ws), "x_in: ")
+    refused(lambda: B.block_forward(shape, ts, w, mod, rope, x, f32(R * H), ws), "x_out: dtype")
+    bad = dict(w, w_o=bf(H * H + 8))
+    refused(lambda: B.block_forward(shape, ts, bad, mod, rope, x, xo, ws), "w_o: ")
+    bad = dict(w, w_fc1=bf(2 * H * sh.ffn).view(2 * sh.ffn, H)[::2])
+    refused(lambda: B.block_forward(shape, ts, bad, mod, rope, x, xo, ws), "w_fc1: not contiguous")
+    q = bf(nh * R * d)
+    refused(lambda: B.routed_attn(shape, ts, q, q, bf(nh * R * d - 64), bf(R * H), ws), "v: ")
+    refused(lambda: B.routed_attn(shape, ts, q, q, q, bf(R * H), ws,
+                                  sel=torch.zeros(3, dtype=torch.int32)), "sel: ")
+    head = {k: bf(int(np.prod(v.shape))).view(v.shape) for k, v in S.head_weights(sh).items()}
+    vv, va = f32(sh.n_video * sh.c_video), f32(sh.n_audio * sh.c_audio)
+    refused(lambda: B.dit_forward(shape, ts, [w, w], head, f32(18 * H), f32(6 * H), rope, x,
+                                  vv, va, ws), "mod: ")
+    refused(lambda: B.dit_forward(shape, ts, [w], head, mod, f32(6 * H), rope, x,
+                                  vv, f32(3), ws), "vel_audio: ")

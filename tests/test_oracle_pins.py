@@ -827,13 +827,15 @@ def test_quantize_weight_int8_rows_from_bf16_bits():
 
 
 def test_check_tile_map_accepts_and_refuses():
-    """A tile map covers rows [0, R) with strictly increasing starts, and its
-    prefix tiles end exactly where the text and audio rows end."""
+    """A tile map covers rows [0, R) with strictly increasing starts, its
+    prefix tiles end exactly where the text and audio rows end, and no tile
+    holds rows of two segments."""
     ts = O.check_tile_map([0, 4, 10, 16, 20], 4, 6, 10, 2)
     np.testing.assert_array_equal(ts, [0, 4, 10, 16, 20])
     for bad, npt in (([0, 4, 4, 16, 20], 2),     # an empty tile
                      ([0, 4, 10, 16, 21], 2),    # does not end at R
                      ([1, 4, 10, 16, 20], 2),    # does not start at 0
-                     ([0, 4, 12, 16, 20], 2)):   # prefix ends inside the audio rows
+                     ([0, 4, 12, 16, 20], 2),    # prefix ends inside the audio rows
+                     ([0, 2, 10, 16, 20], 2)):   # tile [2, 10) holds text and audio rows
         with pytest.raises(AssertionError):
             O.check_tile_map(bad, 4, 6, 10, npt)
