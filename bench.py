@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--blocks", type=int, default=N_BLOCKS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full-block", action="store_true",
+                    help="time the oracle's full-size block whole (minutes of CPU) instead of "
+                         "its all-row part plus a 512-row sample")
     ap.add_argument("--no-prof", action="store_true", help="time without per-kernel events")
     ap.add_argument("--workload", choices=["full", "fasth3"], default="full",
                     help="full: the default 50-block forward (hidden 5120, GELU); fasth3: the "
@@ -385,39 +388,77 @@ def attention_keys(sh, ts, npt):
     return P * sh.rows + sh.n_video * (P + k * mean_vt)
 
 
-def cpu_baseline(sh, ts, npt, n_blocks):
-    """The oracle (as it stands) on one full-size block: q/k/v, head layout
-    and routing over all rows, attention + out projection + MLP over a sample
-    of rows; the sampled part is scaled to all rows, then x n_blocks."""
-    from oracle import h3_oracle as O
-    from audio_diffusion_transformer_amd import synth as S
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    w = S.block_weights(sh)
-    mod = S.modulation(sh)
-    rope = S.rope_tables(sh)
-    x = S.activations(sh, field=True)
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_block_s(C, sh, ts, npt, w, mod, rope, x, rows=None):
+    t = time.perf_counter()
+    C.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows)
+    return time.perf_counter() - t
+
+
+def _config_inputs(sh):
+    from audio_diffusion_transformer_amd import synth as S
+    ts, npt = S.tile_map(sh)
+    return (ts, npt, S.block_weights(sh), S.modulation(sh), S.rope_tables(sh),
+            S.activations(sh, field=True))
+
+
+def cpu_baseline(sh, n_blocks, full_c3=False):
+    """The plain C++ oracle (oracle/h3_ref.cpp, as it stands) timed on this
+    host's cores by wall clock: the tiny block (1,024 rows, hidden 256) with
+    every thread and with one, the mid block (4,608 rows, hidden 3072), and
+    the full-size block (15,435 rows, hidden 5120) -- measured whole with
+    full_c3, else as its all-row part (norm, QKV, head layout, routing) plus
+    attention, out projection and MLP on a stratified sample of 512 rows,
+    scaled to every row.  The 50-block forward is that block time x 50,
+    extrapolated."""
+    from oracle import h3_ref as C
+    from audio_diffusion_transformer_amd import synth as S
+    threads = C.set_threads(0)
+    meas = {}
+    inp = _config_inputs(S.TINY)
+    _oracle_block_s(C, S.TINY, *inp)                     # first call: page in, spin up threads
+    meas["c1_tiny_block_s"] = round(_oracle_block_s(C, S.TINY, *inp), 3)
+    C.set_threads(1)
+    meas["c1_tiny_block_1_thread_s"] = round(_oracle_block_s(C, S.TINY, *inp), 3)
+    C.set_threads(threads)
+    meas["c2_mid_block_s"] = round(_oracle_block_s(C, S.MID, *_config_inputs(S.MID)), 2)
+    ts, npt, w, mod, rope, x = _config_inputs(sh)
     R = sh.rows
-    rng = np.random.default_rng(0)
-    # proportional stratified sample: text/audio and video rows in their share of R
-    n_sample = 512
-    n_dense = int(round(n_sample * sh.n_prefix / R))
-    n_vid = n_sample - n_dense
-    rows = np.sort(np.concatenate([rng.choice(sh.n_prefix, n_dense, replace=False),
-                                   sh.n_prefix + rng.choice(sh.n_video, n_vid, replace=False)]))
-    tm = {}
-    O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows, timings=tm)
-    t_all, t_rows = tm["all_rows"], tm["per_row"]
-    per_block = t_all + t_rows * R / n_sample
+    if full_c3:
+        per_block = _oracle_block_s(C, sh, ts, npt, w, mod, rope, x)
+        meas["c3_full_block_s"] = round(per_block, 2)
+        sample = f"the full-size block measured whole ({per_block:.1f} s)"
+    else:
+        rng = np.random.default_rng(0)
+        n_sample = 512
+        n_dense = int(round(n_sample * sh.n_prefix / R))
+        rows = np.sort(np.concatenate([
+            rng.choice(sh.n_prefix, n_dense, replace=False),
+            sh.n_prefix + rng.choice(sh.n_video, n_sample - n_dense, replace=False)]))
+        t_all = _oracle_block_s(C, sh, ts, npt, w, mod, rope, x, rows=np.zeros(0, np.int64))
+        t_rows = max(_oracle_block_s(C, sh, ts, npt, w, mod, rope, x, rows=rows) - t_all, 0.0)
+        per_block = t_all + t_rows * R / n_sample
+        meas["c3_full_block_all_row_part_s"] = round(t_all, 2)
+        meas["c3_full_block_512_rows_s"] = round(t_rows, 2)
+        meas["c3_full_block_s"] = round(per_block, 2)
+        sample = (f"full-size block: all-row part measured ({t_all:.1f} s), attention + out "
+                  f"projection + MLP on 512 of {R} rows measured ({t_rows:.1f} s) and scaled, "
+                  f"{per_block:.1f} s per block")
     return {
-        "value": per_block * n_blocks, "unit": "s", "cores": int(cores), "kind": "oracle",
-        "sample": (f"one block at {R} rows: norm, QKV, head layout and routing over all rows "
-                   f"({t_all:.1f} s), attention + out projection + MLP over {n_dense} text/audio "
-                   f"and {n_vid} video rows ({t_rows:.1f} s) scaled by {R}/{n_sample}; "
-                   f"per block {per_block:.1f} s, x {n_blocks} blocks (extrapolated)"),
+        "value": round(per_block * n_blocks, 1), "unit": "s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"plain C++ fp32 oracle, {threads} OpenMP threads: {sample}; x {n_blocks} "
+                   f"blocks = the forward (extrapolated)"),
+        "nproc": os.cpu_count(), "cpu_model": _cpu_model(), "measured": meas,
     }
 
 
@@ -507,9 +548,16 @@ def main():
             B.dit_forward_tr(shape, ts, tr, warr, hw, mods[s], mfin[s], rope, x, vv, va, ws,
                              stream=stream)
 
+    # every forward, warm-up ones included, is bracketed by events on the launch
+    # stream: forward 1 is the first after setup (cold), as the pages report
+    # step 1 of their 8-step run apart from the median of steps 2-8
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(args.warmup + 1)]
+    wev[0].record(stream)
     for s in range(args.warmup):
         forward(s)
+        wev[s + 1].record(stream)
     torch.cuda.synchronize()
+    warm_ms = [wev[i].elapsed_time(wev[i + 1]) for i in range(args.warmup)]
     print(f"warmup done ({args.warmup})", file=sys.stderr, flush=True)
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -602,6 +650,13 @@ def main():
                                                    roofline["calibrated_peak"], 4)
 
     srt = sorted(step_ms)
+    seq = (warm_ms + step_ms)[:8]      # the first 8 forwards: an 8-step run, fresh tables each
+    protocol = {"forwards": len(seq), "step1_ms": round(seq[0], 2) if seq else None,
+                "median_steps_2_8_ms": (round(float(np.median(seq[1:])), 2)
+                                        if len(seq) > 1 else None),
+                "note": "step 1 = first forward after setup; steps 2-8 of the same run, each "
+                        "with its own modulation tables (events on the launch stream; steps "
+                        "before the timed region carry no per-kernel events)"}
     line = {
         "metric": ("s per 50-block DiT forward at 15,435 rows; GEMM/attn % of bf16 MFMA peak"
                    if args.workload == "full" else
@@ -637,14 +692,16 @@ def main():
         "determinism": determinism,
         "step_ms": [round(s, 2) for s in step_ms],
         "median_step_s": round(srt[len(srt) // 2] / 1e3, 5),
+        "protocol": protocol,
         "roofline": roofline,
         "calibration": calib,
         "kernels": kernels,
         "prof_events": not args.no_prof,
     }
-    if not args.no_cpu_baseline:
-        print("cpu baseline (oracle on a bounded sample) ...", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(sh, ts, npt, L)
+    if not args.no_cpu_baseline and tr is None and not args.int8:
+        print("cpu baseline (the C++ oracle; tiny, mid and a bounded sample of the full "
+              "block) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(sh, L, full_c3=args.cpu_full_block)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

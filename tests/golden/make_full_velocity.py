@@ -1,0 +1,108 @@
+"""Writes full_velocity_2block.json: the oracle's velocities of a two-block
+forward at the full size (15,435 rows: 512 text / 543 audio / 14,380 video,
+hidden 5,120, 40 x 128 heads, GELU FFN 20,480, tile 64, top-k 32 + pooled)
+on sampled audio and video rows, and the oracle's self-noise floor on the same
+rows.
+
+Calls only oracle/ (the plain C++ oracle) and the seeded input generator.  The
+GPU test tests/test_gpu_velocity.py regenerates the same inputs and compares
+h3_dit_forward's velocities on these rows with the stored ones.
+
+The oracle runs block 1 on every row; block 2 runs its all-row steps (norm,
+QKV, head layout, routing) on every row and its attention and MLP on the
+sampled rows; then the final norm and the heads on those rows (the pages'
+first-forward velocity comparison, "TensorFold PR #949", Receipts: Parity).
+Self-noise: the same computation with the tile-mean and tile-score sums
+reversed (the pages' self-noise rows of the same table), compared with the
+forward one.  Run: python tests/golden/make_full_velocity.py  (a few minutes).
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from audio_diffusion_transformer_amd import synth as S  # noqa: E402
+from oracle import h3_ref as C  # noqa: E402
+
+OUT = os.path.join(HERE, "full_velocity_2block.json")
+L = 2
+SEED = 42
+
+
+def inputs():
+    """The two-block forward's inputs (also used by the GPU test)."""
+    sh = S.FULL
+    ts, npt = S.tile_map(sh)
+    blocks = [S.block_weights(sh, seed=SEED + l) for l in range(L)]
+    mods = np.stack([S.modulation(sh, block=l, seed=SEED) for l in range(L)])
+    head = S.head_weights(sh, seed=SEED)
+    mf = S.final_modulation(sh, seed=SEED)
+    rope = S.rope_tables(sh)
+    x = S.activations(sh, seed=SEED, field=True)
+    return sh, ts, npt, blocks, mods, head, mf, rope, x
+
+
+def sample_rows(sh, ts):
+    """48 video and 24 audio rows: seeded picks plus the first and last rows of
+    each segment and the rows of the ragged last video tile."""
+    rng = np.random.default_rng(SEED)
+    P = sh.n_text + sh.n_audio
+    aud = set(rng.choice(np.arange(sh.n_text, P), 22, replace=False).tolist())
+    aud |= {sh.n_text, P - 1}
+    vid = set(rng.choice(np.arange(P, sh.rows), 44, replace=False).tolist())
+    vid |= {P, int(ts[-2]), int(ts[-2]) + 1, sh.rows - 1}
+    return np.array(sorted(aud)), np.array(sorted(vid))
+
+
+def oracle_velocities(sh, ts, npt, blocks, mods, head, mf, rope, x, rows, reverse):
+    seg = np.where(rows < sh.n_text, 0, np.where(rows < sh.n_text + sh.n_audio, 1, 2))
+    x_bits = x
+    for l in range(L - 1):
+        r = C.block_forward(sh, ts, npt, blocks[l], mods[l], rope, x_bits, reverse=reverse)
+        x_bits = r["x2_bits"]
+    r = C.block_forward(sh, ts, npt, blocks[L - 1], mods[L - 1], rope, x_bits, out_rows=rows,
+                        reverse=reverse)
+    return C.final_heads(sh, r["x2_bits"], seg, mf, head)
+
+
+def _metrics(got, ref):
+    g, r = np.ravel(got), np.ravel(ref)
+    return dict(cos=float(g @ r / (np.linalg.norm(g) * np.linalg.norm(r))),
+                rel=float(np.linalg.norm(g - r) / np.linalg.norm(r)),
+                max_abs=float(np.max(np.abs(g - r))))
+
+
+def main():
+    t0 = time.time()
+    sh, ts, npt, blocks, mods, head, mf, rope, x = inputs()
+    aud, vid = sample_rows(sh, ts)
+    rows = np.concatenate([aud, vid])
+    vv, va = oracle_velocities(sh, ts, npt, blocks, mods, head, mf, rope, x, rows, 0)
+    t1 = time.time()
+    vv_r, va_r = oracle_velocities(sh, ts, npt, blocks, mods, head, mf, rope, x, rows,
+                                   C.REV_MEANS | C.REV_SCORES)
+    out = dict(
+        description="Oracle (plain C++, fp32 ascending sums) velocities of a 2-block forward at "
+                    "15,435 rows (512/543/14,380), hidden 5120, 40x128 heads, GELU FFN 20480, "
+                    "tile 64, top-k 32 + pooled, seed 42, x with the smooth field; written by "
+                    "tests/golden/make_full_velocity.py",
+        audio_rows=aud.tolist(), video_rows=vid.tolist(),
+        vel_audio=[[float(np.float32(v)) for v in r] for r in va],
+        vel_video=[[float(np.float32(v)) for v in r] for r in vv],
+        self_noise=dict(audio=_metrics(va_r, va), video=_metrics(vv_r, vv)),
+        oracle_seconds=round(t1 - t0, 1), threads=C.set_threads(0))
+    with open(OUT, "w") as f:
+        json.dump(out, f, indent=0)
+    print("wrote", OUT, "self-noise", out["self_noise"], "oracle s", out["oracle_seconds"])
+
+
+if __name__ == "__main__":
+    main()

@@ -93,45 +93,5 @@ def run_routed(sh, ts, npt, q, k, v):
                 scores=scores.cpu().numpy()[:, :nQ].astype(np.float64))
 
 
-def close_bf16(got, ref, ulps=2.0, atol=1e-5, frac_1ulp=1e-3):
-    """Every element within `ulps` bf16 spacings of the reference plus `atol`,
-    and at most a fraction `frac_1ulp` of the elements more than one spacing
-    away.  Returns the worst excess over the elementwise bar (<= 0 passes);
-    a violated fraction is reported as a positive excess too."""
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    if got.size == 0:
-        return 0.0
-    err = np.abs(got - ref)
-    ulp = P.bf16_ulp(ref)
-    worst = float(np.max(err - ulps * ulp - atol))
-    frac = float(np.mean(err > ulp + 1e-12))
-    if worst > 0 or frac > frac_1ulp:
-        print(f"close_bf16: worst excess {worst:.3g}, fraction beyond 1 spacing {frac:.3g}",
-              flush=True)
-        return max(worst, frac - frac_1ulp)
-    return worst
-
-
-class Checks:
-    """Collects every comparison of a case, prints them all, then asserts."""
-
-    def __init__(self, case):
-        self.case = case
-        self.failed = []
-        self.lines = []
-
-    def close(self, name, got, ref, **kw):
-        ex = close_bf16(got, ref, **kw)
-        self.lines.append(f"{name}: excess {ex:.3g}")
-        if ex > 0:
-            self.failed.append(name)
-
-    def true(self, name, cond, info=""):
-        self.lines.append(f"{name}: {'ok' if cond else 'FAIL'} {info}")
-        if not cond:
-            self.failed.append(name)
-
-    def done(self):
-        print(f"[{self.case}] " + "; ".join(self.lines), flush=True)
-        assert not self.failed, f"{self.case}: failed {self.failed}"
+close_bf16 = P.close_bf16
+Checks = P.Checks

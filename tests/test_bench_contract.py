@@ -54,3 +54,5 @@ def test_one_block_line_carries_the_contract_fields():
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert rf["traffic"] is None or rf["traffic"] > 0
     assert d["determinism"]["identical"] is True
+    pr = d["protocol"]
+    assert pr["forwards"] == 1 and pr["step1_ms"] > 0 and pr["median_steps_2_8_ms"] is None

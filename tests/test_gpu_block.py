@@ -1,8 +1,9 @@
 """GPU parity of h3_block_forward against the CPU oracle, stage by stage,
 on seeded inputs (tiny workload and edge shapes).
 
-Tolerances, from the arithmetic: the oracle carries float64 and rounds only
-at the bf16 points; the GPU sums in fp32 in another order.  A bf16 result can
+Tolerances, from the arithmetic: the oracle (the plain C++ one) sums in fp32
+in ascending order and rounds at the bf16 points; the GPU sums in fp32 in
+another order.  A bf16 result can
 therefore land one spacing away where the exact value sits next to a rounding
 boundary, and one such flip upstream can move a downstream value by another
 spacing: elementwise bars are 2 bf16 spacings plus a small absolute floor
@@ -16,7 +17,7 @@ import pytest
 import torch
 
 from audio_diffusion_transformer_amd import synth as S
-from oracle import h3_oracle as O
+from oracle import h3_ref as O
 
 import gpu_harness as G
 import parity as P
@@ -43,41 +44,14 @@ def _check_block(sh, ts, npt, w, mod, rope, x, strict_sel=True, h_frac=2e-2, v_a
     g = run.read()
     r = O.block_forward(sh, ts, npt, w, mod, rope, x)
     c = G.Checks(case)
-    # a flip of one upstream bf16 value (norm output, QKV product) moves the
-    # normalised, rotated q/k by up to ~one spacing of the row's largest entry
-    c.close("q", g["q"], r["q"], atol=2 ** -5)
-    c.close("k", g["k"], r["k"], atol=2 ** -5)
-    c.close("v", g["v"], r["v"], atol=v_atol)
-    nQ = len(ts) - 1 - npt
-    if nQ > 0:
-        for name in ("qbar", "kbar", "vbar"):
-            c.true(name, np.max(np.abs(g[name] - r[name])) < 2 ** -8,
-                   f"{np.max(np.abs(g[name] - r[name])):.3g}")
-        c.true("scores", np.max(np.abs(g["scores"] - r["scores"])) < 1e-3,
-               f"{np.max(np.abs(g['scores'] - r['scores'])):.3g}")
-        checked, bad, skipped = P.selection_agrees(g["sel"], r["sel"], r["scores"], npt, sh.top_k)
-        c.true("sel", bad == 0 and (not strict_sel or checked >= 0.9 * (checked + skipped)),
-               f"checked {checked} bad {bad} skipped {skipped}")
-        c.true("sel order", bool(np.all(np.diff(g["sel"], axis=-1) > 0)))
-        c.true("sel range", bool(np.all((g["sel"] >= npt) & (g["sel"] < len(ts) - 1))))
-        if sh.pooled:
-            c.true("pooled", np.max(np.abs(g["pooled"] - r["pooled"])) < 1e-3,
-                   f"{np.max(np.abs(g['pooled'] - r['pooled'])):.3g}")
+    P.block_checks(c, g, r, npt, len(ts) - 1, sh.top_k, sh.pooled, strict_sel=strict_sel,
+                   h_frac=h_frac, v_atol=v_atol)
     # padded rows of the head-major operands are zero
     tp = P.padded_starts(ts)
     pads_zero = all(not g["q_pad"][:, tp[t] + ts[t + 1] - ts[t]:tp[t + 1]].any() and
                     not g["vt_pad"][:, :, tp[t] + ts[t + 1] - ts[t]:tp[t + 1]].any()
                     for t in range(len(ts) - 1))
     c.true("padding", pads_zero)
-    m = P.metrics(g["attn"], r["attn"])
-    c.true("attn metrics", m["cos"] > 0.99999 and m["rel"] < 4e-3, str(m))
-    c.true("attn elementwise",
-           bool(np.all(np.abs(g["attn"] - r["attn"]) <= 4e-3 + 2 ** -7 * np.abs(r["attn"]))))
-    for name in ("x1", "n2", "h", "x2"):
-        c.close(name, g[name], r[name], ulps=2, atol=2 ** -6,
-                frac_1ulp=h_frac if name == "h" else 2e-2)
-    m = P.metrics(g["x2"], r["x2"])
-    c.true("x2 metrics", m["cos"] > 0.9999 and m["rel"] < 1e-3, str(m))
     c.done()
     return run, g, r
 
@@ -201,6 +175,8 @@ def test_block_at_size_limits():
            f"{np.max(np.abs(g['scores'] - r['scores'])):.3g}")
     checked, bad, skipped = P.selection_agrees(g["sel"], r["sel"], r["scores"], npt, sh.top_k)
     c.true("sel", bad == 0 and checked > 0, f"checked {checked} bad {bad} skipped {skipped}")
+    own = P.selection_follows_scores(g["sel"], g["scores"], npt, sh.top_k)
+    c.true("sel = rule top-k of own scores", own == 0, f"{own} rows differ")
     c.true("sel order", bool(np.all(np.diff(g["sel"], axis=-1) > 0)))
     c.true("pooled", np.max(np.abs(g["pooled"] - r["pooled"])) < 1e-3,
            f"{np.max(np.abs(g['pooled'] - r['pooled'])):.3g}")

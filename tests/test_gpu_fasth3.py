@@ -11,7 +11,7 @@ import torch
 from audio_diffusion_transformer_amd import binding as B
 from audio_diffusion_transformer_amd import synth as S
 from audio_diffusion_transformer_amd import tensors as T
-from oracle import h3_oracle as O
+from oracle import h3_ref as O
 
 import gpu_harness as G
 import parity as P
@@ -115,6 +115,8 @@ def test_fasth3_full_size_block_sampled_rows():
     checked, bad, skipped = P.selection_agrees(g["sel"], r["sel"], r["scores"], npt, sh.top_k)
     c.true("sel", bad == 0 and checked >= 0.5 * (checked + skipped),
            f"checked {checked} bad {bad} skipped {skipped}")
+    own = P.selection_follows_scores(g["sel"], g["scores"], npt, sh.top_k)
+    c.true("sel = rule top-k of own scores", own == 0, f"{own} rows differ")
     m = P.metrics(g["attn"][rows], r["attn"])
     c.true("attn", m["cos"] > 0.99999 and m["rel"] < 4e-3, str(m))
     for name in ("x1", "n2", "x2"):

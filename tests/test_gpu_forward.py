@@ -11,7 +11,8 @@ import torch
 from audio_diffusion_transformer_amd import binding as B
 from audio_diffusion_transformer_amd import synth as S
 from audio_diffusion_transformer_amd import tensors as T
-from oracle import h3_oracle as O
+from oracle import h3_oracle as O64
+from oracle import h3_ref as O
 
 import gpu_harness as G
 import parity as P
@@ -54,10 +55,13 @@ def test_tiny_forward_velocities(L):
     vv, va = _run_forward(sh, *inp)
     ts, npt, blocks, head, mods, mf, rope, x = inp
     r = O.dit_forward(sh, ts, npt, blocks, head, mods, mf, rope, x)
-    for got, ref in ((vv, r["vel_video"]), (va, r["vel_audio"])):
-        m = P.metrics(got, ref)
+    # the float64 oracle as a second, independent reference
+    r64 = O64.dit_forward(sh, ts, npt, blocks, head, mods, mf, rope, x)
+    for got, ref, ref64 in ((vv, r["vel_video"], r64["vel_video"]),
+                            (va, r["vel_audio"], r64["vel_audio"])):
         # the stated bar is cos >= 0.998 and rel <= 0.06; a few blocks stay far inside it
-        assert m["cos"] >= 0.9999 and m["rel"] <= 5e-3, m
+        for m in (P.metrics(got, ref), P.metrics(got, ref64)):
+            assert m["cos"] >= 0.9999 and m["rel"] <= 5e-3, m
 
 
 def test_tiny_forward_50_blocks():
@@ -138,6 +142,8 @@ def test_full_size_block_sampled_rows():
     checked, bad, skipped = P.selection_agrees(g["sel"], r["sel"], r["scores"], npt, sh.top_k)
     c.true("sel", bad == 0 and checked >= 0.8 * (checked + skipped),
            f"checked {checked} bad {bad} skipped {skipped}")
+    own = P.selection_follows_scores(g["sel"], g["scores"], npt, sh.top_k)
+    c.true("sel = rule top-k of own scores", own == 0, f"{own} rows differ")
     m = P.metrics(g["attn"][rows], r["attn"])
     c.true("attn", m["cos"] > 0.99999 and m["rel"] < 4e-3, str(m))
     for name in ("x1", "n2", "x2"):
