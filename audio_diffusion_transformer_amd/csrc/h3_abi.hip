@@ -21,6 +21,9 @@
 #include <string>
 #include <vector>
 
+#include <algorithm>
+#include <functional>
+
 #include "common.h"
 #include "internal.h"
 
@@ -45,6 +48,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
   h3_shape s;
   int R, P, H, D, F, nh, nT, npt, nQ, nsel, Rp, n_chunks, n_prefix_chunks, nqb, nqb_dense;
+  int max_list;  // longest video key list in 32-row chunks: prefix + the nsel largest tiles
   int A;      // attention width n_heads * head_dim
   int parts;  // blocks per head in the QKV product: 3, or 4 with the routing gate
   int F1;     // FC1 output width: F (GELU) or 2F (SwiGLU)
@@ -126,6 +130,13 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
   p.Rp = p.tpstart[p.nT];
   p.n_chunks = p.Rp / 32;
   p.n_prefix_chunks = p.tpstart[p.npt] / 32;
+  {
+    std::vector<int> vc;
+    for (int t = p.npt; t < p.nT; ++t) vc.push_back((p.tpstart[t + 1] - p.tpstart[t]) / 32);
+    std::sort(vc.begin(), vc.end(), std::greater<int>());
+    p.max_list = p.n_prefix_chunks;
+    for (int e = 0; e < p.nsel && e < (int)vc.size(); ++e) p.max_list += vc[e];
+  }
   if (!attn_shape_ok(p.n_chunks, p.nsel)) return fail(H3_EUNSUPPORTED, "too many key chunks");
   p.chunk_valid.assign(p.n_chunks, 0);
   for (int t = 0; t < p.nT; ++t) {
@@ -293,6 +304,7 @@ int run_attention(const Plan& p, void* ws, int32_t* sel_out, float* scores_out, 
   a.k = at<bf16_t>(ws, p.lay.k);
   a.vt = at<bf16_t>(ws, p.lay.vt);
   a.sel = sel;
+  a.scores = scores;
   a.pooled = p.s.pooled ? at<float>(ws, p.lay.pooled) : nullptr;
   a.tpstart = at<int>(ws, p.off_tpstart);
   a.chunk_valid = at<int>(ws, p.off_chunk);
@@ -312,6 +324,7 @@ int run_attention(const Plan& p, void* ws, int32_t* sel_out, float* scores_out, 
   a.nqb_dense = p.nqb_dense;
   a.n_prefix_chunks = p.n_prefix_chunks;
   a.n_chunks = p.n_chunks;
+  a.max_list = p.max_list;
   prof_begin(H3_K_ATTN, st);
   H3_TRY(launch_attn(p.D, a, st));
   prof_end(H3_K_ATTN, st);

@@ -101,6 +101,7 @@ struct AttnArgs {
   const bf16_t* k;          // [nh][Rp][d]
   const bf16_t* vt;         // [nh][d][Rp]
   const int* sel;           // [nh][nQ][nsel]
+  const float* scores;      // [nh][nQ][nT]: the tile scores (visiting order of the tiles)
   const float* pooled;      // [nh][nQ][d] or null
   const int* tpstart;       // [nT+1]
   const int* chunk_valid;   // [Rp/32]
@@ -110,6 +111,7 @@ struct AttnArgs {
                             // gate[r * gate_stride + h * gate_hstride + c]
   int gate_stride, gate_hstride;
   int nh, Rp, A, nT, npt, nQ, nsel, nqb, nqb_dense, n_prefix_chunks, n_chunks;
+  int max_list;             // longest video key list in chunks (prefix + nsel largest tiles)
 };
 bool attn_shape_ok(int n_chunks, int nsel);
 // matrix-core calibration: n_blocks x 4 waves x iters x 16 bf16 products

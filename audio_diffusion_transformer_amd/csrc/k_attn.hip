@@ -114,12 +114,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   constexpr int SO = D + 4;    // fp32 row stride of the output staging
   constexpr int RING = 2 * STG * 2, OSTG = 64 * SO * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[RING > OSTG ? RING : OSTG];
-  // dynamic: chunk starts and key-list offsets of the selected tiles, then the
+  // dynamic: the selected tiles' scores, chunk starts and key-list offsets (in
+  // visiting order), the key list of a video block as chunk ids, then the
   // valid-row counts of every chunk
   extern __shared__ __attribute__((aligned(16))) int dyn[];
-  int* const sOff = dyn;                    // [nsel + 1]
-  int* const sC0 = dyn + a.nsel + 1;        // [nsel]
-  uint8_t* const sValid = reinterpret_cast<uint8_t*>(dyn + 2 * a.nsel + 1);  // [n_chunks]
+  float* const sKey = reinterpret_cast<float*>(dyn);          // [nsel]
+  int* const sC0 = dyn + a.nsel;                              // [nsel]
+  int* const sOff = dyn + 2 * a.nsel;                         // [nsel + 1]
+  uint16_t* const sList = reinterpret_cast<uint16_t*>(dyn + 3 * a.nsel + 1);  // [max_list]
+  uint8_t* const sValid = reinterpret_cast<uint8_t*>(sList + a.max_list);     // [n_chunks]
   bf16_t* const ring = reinterpret_cast<bf16_t*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -159,24 +162,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
   for (int c = tid; c < a.n_chunks; c += 256) sValid[c] = (uint8_t)a.chunk_valid[c];
 
-  // Key list: every chunk (dense rows), or the prefix chunks followed by the
-  // chunks of the selected tiles in ascending tile order (video rows).
+  // Key list: every chunk in order (dense rows); for video rows the chunks of
+  // the selected tiles, the best-scoring tile first, then the prefix chunks.
+  // The attention output does not depend on the order (each weight is taken
+  // against the running max and rescaled with it); visiting the tiles the
+  // routing ranks highest first settles the running max early, so later
+  // chunks rarely rescale the accumulators.  When every video tile is
+  // selected the list is the dense one, in the same ascending order, so a
+  // routed call with all tiles gives the dense call's bytes.
   int nchunk;
   if (dense) {
     nchunk = a.n_chunks;
     __syncthreads();
   } else {
-    // Selected tiles -> chunk starts and chunk counts, all entries in
-    // parallel; then an exclusive scan of the counts (wave 0, shuffles).
-    const int* sel = a.sel + ((size_t)h * a.nQ + (tile - a.npt)) * a.nsel;
+    const int qt = tile - a.npt;
+    const int* sel = a.sel + ((size_t)h * a.nQ + qt) * a.nsel;
+    const bool ranked = a.nsel < a.nQ;
+    if (ranked) {
+      const float* srow = a.scores + ((size_t)h * a.nQ + qt) * a.nT;
+      for (int e = tid; e < a.nsel; e += 256) {
+        const float v = srow[sel[e]];
+        sKey[e] = v != v ? -INFINITY : v;  // NaN ranks as -inf
+      }
+      __syncthreads();
+    }
+    // entry e goes to position r: by descending score, ties in selection order
+    // (ascending tile); with every tile selected, r = e
     for (int e = tid; e < a.nsel; e += 256) {
+      int r = e;
+      if (ranked) {
+        const float v = sKey[e];
+        r = 0;
+        for (int j = 0; j < a.nsel; ++j) {
+          const float w = sKey[j];
+          r += (w > v) || (w == v && j < e);
+        }
+      }
       const int t = sel[e];
       const int p0 = a.tpstart[t], p1 = a.tpstart[t + 1];
-      sC0[e] = p0 >> 5;
-      sOff[e] = (p1 - p0) >> 5;
+      sC0[r] = p0 >> 5;
+      sOff[r] = (p1 - p0) >> 5;
     }
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 0) {  // exclusive scan of the chunk counts (wave 0, shuffles)
       const int per = (a.nsel + 63) >> 6;  // entries per lane
       int lsum = 0;
       for (int j = 0; j < per; ++j) {
@@ -189,7 +217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         const int y = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += y;
       }
-      int run = a.n_prefix_chunks + incl - lsum;
+      int run = incl - lsum;
       for (int j = 0; j < per; ++j) {
         const int e = lane * per + j;
         if (e < a.nsel) {
@@ -201,16 +229,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       if (lane == 63) sOff[a.nsel] = run;
     }
     __syncthreads();
-    nchunk = sOff[a.nsel];
+    // flat list of chunk ids: ranked tiles' chunks, then the prefix chunks
+    // (ascending order with every tile selected: prefix first, like dense)
+    const int nsc = sOff[a.nsel];
+    const int base_sel = ranked ? 0 : a.n_prefix_chunks;
+    const int base_pre = ranked ? nsc : 0;
+    for (int e = tid; e < a.nsel; e += 256)
+      for (int c = 0; c < sOff[e + 1] - sOff[e]; ++c)
+        sList[base_sel + sOff[e] + c] = (uint16_t)(sC0[e] + c);
+    for (int c = tid; c < a.n_prefix_chunks; c += 256) sList[base_pre + c] = (uint16_t)c;
+    nchunk = nsc + a.n_prefix_chunks;
+    __syncthreads();
   }
-  // Position ci of the key list -> chunk id.  ci only grows, so the selected
-  // entry holding it is tracked forward.
-  int ent = 0;
-  auto chunk_at = [&](int ci) -> int {
-    if (dense || ci < a.n_prefix_chunks) return ci;
-    while (sOff[ent + 1] <= ci) ++ent;
-    return sC0[ent] + (ci - sOff[ent]);
-  };
+  auto chunk_at = [&](int ci) -> int { return dense ? ci : (int)sList[ci]; };
 
   const size_t Rp = (size_t)a.Rp;
   const int l16 = lane & 15, g = lane >> 4;
@@ -390,7 +421,8 @@ bool attn_shape_ok(int n_chunks, int nsel) { return n_chunks <= kMaxChunks && ns
 
 hipError_t launch_attn(int head_dim, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.nqb * a.nh), block(256);
-  const size_t dyn = sizeof(int) * (2 * (size_t)a.nsel + 1) + (size_t)a.n_chunks;
+  const size_t dyn = sizeof(int) * (3 * (size_t)a.nsel + 1) + 2 * (size_t)a.max_list +
+                     (size_t)a.n_chunks;
   if (head_dim == 128) hipLaunchKernelGGL(k_attn<128>, grid, block, dyn, s, a);
   else hipLaunchKernelGGL(k_attn<64>, grid, block, dyn, s, a);
   return hipGetLastError();

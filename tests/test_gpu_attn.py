@@ -7,7 +7,8 @@ import torch
 
 from audio_diffusion_transformer_amd import binding as B
 from audio_diffusion_transformer_amd import synth as S
-from oracle import h3_ref as O
+from oracle import h3_oracle as O
+from oracle import h3_ref as O32
 
 import gpu_harness as G
 import parity as P
@@ -27,8 +28,11 @@ def _check(sh, rows=None, seed=42, amp=1.0):
     q, k, v = S.attn_qkv(sh, seed=seed, amp=amp)
     g = G.run_routed(sh, ts, npt, q, k, v)
     r = O.routed_attn(sh, ts, npt, q, k, v, rows=rows)
+    r32 = O32.routed_attn(sh, ts, npt, q, k, v, rows=rows)
     c = P.Checks(f"routed R={sh.rows} tile={sh.tile} k={sh.top_k}")
+    # elementwise against the float64 oracle, whole tensors against the fp32 one
     P.routed_checks(c, g, r, npt, sh.top_k, rows=rows)
+    P.fp32_oracle_checks(c, g, r32, ("out",), npt, sh.top_k, rows=rows)
     c.done()
     return g, r, ts, npt, q, k, v
 
@@ -93,10 +97,12 @@ def test_topk_nan_scores_rank_last():
 
 
 def softmax_probe_inputs(sh, seed=3):
-    """Every query row's largest score sits at key row 0 (a text row, first in
-    every key list): q rows (8, 0, ...), k row 0 (1.5, 0, ...), all other k
-    rows (0.296875, 0, ...), so the other weights are e^-1.203125 = 0.30024,
-    which bf16 rounds up to 0.30078125; v ~ N(0, 1)."""
+    """Every query row's largest score sits in the first key chunk it visits:
+    q rows (8, 0, ...); k rows 0 (first of the dense rows' list) and P (the
+    first video row: its tile has the highest tile score, so the video rows
+    visit it first) are (1.5, 0, ...), all other k rows (0.296875, 0, ...), so
+    the other weights are e^-1.203125 = 0.30024, which bf16 rounds up to
+    0.30078125; v ~ N(0, 1)."""
     nh, R, d = sh.n_heads, sh.rows, sh.head_dim
     one = lambda x: np.uint16(np.float32(x).view(np.uint32) >> 16)
     q = np.zeros((nh, R, d), np.uint16)
@@ -104,6 +110,7 @@ def softmax_probe_inputs(sh, seed=3):
     q[:, :, 0] = one(8.0)
     k[:, :, 0] = one(0.296875)
     k[:, 0, 0] = one(1.5)
+    k[:, sh.n_text + sh.n_audio, 0] = one(1.5)
     v = S.normal_bf16("test.probe.v", (nh, R, d), 1.0, seed=seed)
     return q, k, v
 
@@ -120,7 +127,7 @@ def test_softmax_rounding_points_probe():
     ts, npt = S.tile_map(sh)
     q, k, v = softmax_probe_inputs(sh)
     g = G.run_routed(sh, ts, npt, q, k, v)
-    r = O.routed_attn(sh, ts, npt, q, k, v)
+    r = O32.routed_attn(sh, ts, npt, q, k, v)
     c = P.Checks("softmax probe")
     P.rounding_probe_checks(c, g["out_bits"], r["out_bits"])
     c.done()

@@ -1,9 +1,11 @@
 """GPU parity of h3_block_forward against the CPU oracle, stage by stage,
 on seeded inputs (tiny workload and edge shapes).
 
-Tolerances, from the arithmetic: the oracle (the plain C++ one) sums in fp32
-in ascending order and rounds at the bf16 points; the GPU sums in fp32 in
-another order.  A bf16 result can
+Two oracles.  The stage-by-stage elementwise bars are taken against the
+float64 oracle; the plain C++ fp32 oracle (the contracted one) is checked at
+whole-tensor bars (parity.fp32_oracle_checks).  Tolerances, from the
+arithmetic: the float64 oracle rounds only at the bf16 points; the GPU sums in
+fp32 in another order.  A bf16 result can
 therefore land one spacing away where the exact value sits next to a rounding
 boundary, and one such flip upstream can move a downstream value by another
 spacing: elementwise bars are 2 bf16 spacings plus a small absolute floor
@@ -17,7 +19,8 @@ import pytest
 import torch
 
 from audio_diffusion_transformer_amd import synth as S
-from oracle import h3_ref as O
+from oracle import h3_oracle as O
+from oracle import h3_ref as O32
 
 import gpu_harness as G
 import parity as P
@@ -46,6 +49,9 @@ def _check_block(sh, ts, npt, w, mod, rope, x, strict_sel=True, h_frac=2e-2, v_a
     c = G.Checks(case)
     P.block_checks(c, g, r, npt, len(ts) - 1, sh.top_k, sh.pooled, strict_sel=strict_sel,
                    h_frac=h_frac, v_atol=v_atol)
+    r32 = O32.block_forward(sh, ts, npt, w, mod, rope, x)
+    P.fp32_oracle_checks(c, g, r32, ("q", "k", "v", "attn", "x1", "h", "x2"), npt,
+                         sh.top_k if len(ts) - 1 > npt else None)
     # padded rows of the head-major operands are zero
     tp = P.padded_starts(ts)
     pads_zero = all(not g["q_pad"][:, tp[t] + ts[t + 1] - ts[t]:tp[t + 1]].any() and

@@ -11,7 +11,8 @@ import torch
 from audio_diffusion_transformer_amd import binding as B
 from audio_diffusion_transformer_amd import synth as S
 from audio_diffusion_transformer_amd import tensors as T
-from oracle import h3_ref as O
+from oracle import h3_oracle as O
+from oracle import h3_ref as O32
 
 import gpu_harness as G
 import parity as P
@@ -106,7 +107,11 @@ def test_fasth3_full_size_block_sampled_rows():
                                      np.arange(R - 40, R)]))
     print("oracle ...", flush=True)
     r = O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows)
+    r32 = O32.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows)
     c = G.Checks("fasth3 full-size block")
+    # elementwise against the float64 oracle, whole tensors against the fp32 one
+    P.fp32_oracle_checks(c, g, r32, ("q", "k", "v", "attn", "x1", "h", "x2"), npt, sh.top_k,
+                         rows=rows)
     c.close("q", g["q"], r["q"], atol=2 ** -5)
     c.close("k", g["k"], r["k"], atol=2 ** -5)
     c.close("v", g["v"], r["v"], atol=2 ** -9)

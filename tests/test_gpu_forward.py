@@ -133,8 +133,12 @@ def test_full_size_block_sampled_rows():
                                      np.arange(1055, 1055 + 64), np.arange(8000, 8070),
                                      np.arange(R - 50, R)]))
     print("oracle ...", flush=True)
-    r = O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows)
+    r = O64.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows)
+    r32 = O.block_forward(sh, ts, npt, w, mod, rope, x, out_rows=rows)
     c = G.Checks("full-size block")
+    # elementwise against the float64 oracle, whole tensors against the fp32 one
+    P.fp32_oracle_checks(c, g, r32, ("q", "k", "v", "attn", "x1", "h", "x2"), npt, sh.top_k,
+                         rows=rows)
     c.close("q", g["q"], r["q"], atol=2 ** -5)
     c.close("k", g["k"], r["k"], atol=2 ** -5)
     # K = 5120: fp32 sums and upstream flips move a product by up to ~2^-9
