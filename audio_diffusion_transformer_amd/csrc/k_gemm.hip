@@ -383,8 +383,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
   }
   // Gated residual: this lane's residual chunks (the output chunks it writes
   // below) are loaded before the staging, so that their latency passes under it.
-  u32x4_t xres[2 * NI];
-  if constexpr (EPI == EPI_BIAS_RESGATE) {
+  // The int8 form holds the int32 sums and their scales too and would spill
+  // with these 64 registers live, so it loads each chunk where it is used.
+  constexpr bool kResEarly = EPI == EPI_BIAS_RESGATE && !I8;
+  u32x4_t xres[kResEarly ? 2 * NI : 1];
+  if constexpr (kResEarly) {
 #pragma unroll
     for (int t = 0; t < 2 * NI; ++t) {
       const int q = (t + 2 * ib) * 64 + lane;
@@ -420,7 +423,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + r * 64 + c8);
     const size_t o = (size_t)row * N + col;
     if constexpr (EPI == EPI_BIAS_RESGATE) {
-      const u32x4_t x = xres[t];
+      u32x4_t x;
+      if constexpr (kResEarly) x = xres[t];
+      else x = *reinterpret_cast<const u32x4_t*>(ep.res + o);
       const float* gp =
           ep.gate + (size_t)seg_of(row, ep.n_text, ep.n_prefix) * ep.gate_seg_stride + col;
       const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
