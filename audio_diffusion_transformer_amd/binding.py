@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libh3.so")
 
 H3_OK, H3_EINVAL, H3_EWORKSPACE, H3_EHIP, H3_EUNSUPPORTED = 0, -1, -2, -3, -4
 H3_WS_BLOCK, H3_WS_DIT, H3_WS_ATTN, H3_WS_DIT_I8 = 0, 1, 2, 3
-ABI_VERSION = 4  # must match H3_ABI_VERSION in include/h3.h
+ABI_VERSION = 5  # must match H3_ABI_VERSION in include/h3.h
 
 KERNEL_CLASSES = ["modnorm", "gemm_qkv", "heads", "route", "attn", "gemm_o", "gemm_fc1",
                   "gemm_fc2", "final", "tables", "rows_in", "time", "euler", "tokens", "quant"]
@@ -114,6 +114,8 @@ def lib():
     L.h3_modulation.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32,
                                 ctypes.POINTER(H3TimeWeights), f32p, _vp, _vp, _vp,
                                 ctypes.c_size_t, _vp]
+    L.h3_modulation_noalloc.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32,
+                                        ctypes.POINTER(H3TimeWeights), f32p, _vp, _vp, _vp]
     L.h3_denoise_workspace_bytes.argtypes = [ctypes.POINTER(H3Shape), i32p, ctypes.c_int32]
     L.h3_denoise_workspace_bytes.restype = ctypes.c_size_t
     L.h3_denoise.argtypes = [ctypes.POINTER(H3Shape), ctypes.c_int32, ctypes.c_int32, i32p,
@@ -140,7 +142,8 @@ def lib():
     L.h3_prof_kernel_name.restype = ctypes.c_char_p
     L.h3_calibrate_mfma.argtypes = [_vp, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
     for f in (L.h3_workspace_layout, L.h3_block_forward, L.h3_dit_forward, L.h3_routed_attn,
-              L.h3_rows_in, L.h3_modulation, L.h3_denoise, L.h3_dit_forward_tr,
+              L.h3_rows_in, L.h3_modulation, L.h3_modulation_noalloc, L.h3_denoise,
+              L.h3_dit_forward_tr,
               L.h3_quantize_rows, L.h3_dit_forward_i8,
               L.h3_prof_enable, L.h3_prof_read):
         f.restype = ctypes.c_int
@@ -429,6 +432,19 @@ def modulation(shape, n_blocks, tw, sigma3, mod, mod_final, ws, stream=None):
     _check(lib().h3_modulation(ctypes.byref(shape), n_blocks, ctypes.byref(tws), sp, _ptr(mod),
                                _ptr(mod_final), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)))
+
+
+def modulation_noalloc(shape, n_blocks, tw, sigma3, mod, mod_final, stream=None):
+    """h3_modulation with the library's static scratch (no workspace argument)."""
+    D, _expect = _Dims(shape), _Checks()
+    _check_time_weights(_expect, tw, D, n_blocks)
+    _expect(mod, "mod", n_blocks * 3 * 6 * D.H, "f32", optional=n_blocks == 0)
+    _expect(mod_final, "mod_final", 3 * 2 * D.H, "f32")
+    _expect.done()
+    tws = time_weights_struct(tw) if isinstance(tw, dict) else tw
+    sg, sp = _f32_host(sigma3)
+    _check(lib().h3_modulation_noalloc(ctypes.byref(shape), n_blocks, ctypes.byref(tws), sp,
+                                       _ptr(mod), _ptr(mod_final), _stream(stream)))
 
 
 def denoise_workspace_bytes(shape, tile_start, n_blocks):

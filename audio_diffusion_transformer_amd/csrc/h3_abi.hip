@@ -18,6 +18,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -768,6 +769,43 @@ void prof_end(int cls, hipStream_t s) {
 
 using namespace h3;
 
+// Scratch of h3_modulation_noalloc, for callers that cannot allocate: the time
+// embedder's hidden and conditioning vectors of the three segments, [3][H] and
+// [3][H] fp32, for H up to the library's hidden limit.  One copy per GPU, held
+// until the process ends; every call on a GPU shares it.
+constexpr int kModScratchHidden = 8192;
+static __device__ __align__(256) float scratch[6 * kModScratchHidden];
+
+namespace h3 {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, taken once per device
+// with hipGetSymbolAddress (in host code the array's name is only a host-side
+// stand-in, never a device address).
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(H3_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(H3_EUNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(H3_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return H3_OK;
+}
+
+}  // namespace
+}  // namespace h3
+
 extern "C" {
 
 int h3_abi_version(void) { return H3_ABI_VERSION; }
@@ -852,6 +890,24 @@ int h3_modulation(const h3_shape* shape, int32_t n_blocks, const h3_time_weights
   if (ws_bytes < need) return fail(H3_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   return run_modulation(shape->hidden, n_blocks, tw, sigma3, mod, mod_final,
                         static_cast<float*>(ws), (hipStream_t)stream);
+}
+
+int h3_modulation_noalloc(const h3_shape* shape, int32_t n_blocks, const h3_time_weights* tw,
+                          const float* sigma3, float* mod, float* mod_final, void* stream) {
+  if (!shape) return fail(H3_EINVAL, "shape is NULL");
+  if (shape->hidden > kModScratchHidden)
+    return fail(H3_EUNSUPPORTED, "hidden %d exceeds the static scratch (hidden <= %d)",
+                shape->hidden, kModScratchHidden);
+  if (h3_modulation_workspace_bytes(shape) == 0) return H3_EINVAL;
+  if (n_blocks < 0) return fail(H3_EINVAL, "n_blocks < 0");
+  if (!sigma3) return fail(H3_EINVAL, "sigma3 is NULL");
+  int rc;
+  if ((rc = check_time_weights(tw, n_blocks))) return rc;
+  if ((n_blocks > 0 && !mod) || !mod_final) return fail(H3_EINVAL, "mod and mod_final are required");
+  float* sc = nullptr;
+  if ((rc = scratch_on_current_device(&sc))) return rc;
+  return run_modulation(shape->hidden, n_blocks, tw, sigma3, mod, mod_final, sc,
+                        (hipStream_t)stream);
 }
 
 int h3_rows_in(const h3_shape* shape, const h3_rows_in_weights* w, const h3_bf16* text_rows,

@@ -25,7 +25,8 @@
  *   - The library allocates no device memory and keeps no pointer after it
  *     returns.  Scratch lives in the caller's workspace `ws` (256-byte
  *     aligned, at least h3_workspace_bytes() bytes).  Concurrent calls need
- *     distinct workspaces.
+ *     distinct workspaces.  (One exception, h3_modulation_noalloc: its
+ *     scratch is a static device array of the library, see there.)
  *   - Outputs must not alias inputs.  Pointers must be 16-byte aligned.
  *   - Same inputs on the same device give byte-identical outputs (no float
  *     atomics; every reduction has a fixed order).
@@ -61,7 +62,7 @@ enum {
 
 enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2, H3_WS_DIT_I8 = 3 };
 
-#define H3_ABI_VERSION 4
+#define H3_ABI_VERSION 5
 
 typedef struct {
   int32_t n_text, n_audio, n_video;  /* packed in this order */
@@ -224,6 +225,18 @@ size_t h3_modulation_workspace_bytes(const h3_shape* shape);
 int h3_modulation(const h3_shape* shape, int32_t n_blocks, const h3_time_weights* tw,
                   const float* sigma3, float* mod, float* mod_final, void* ws, size_t ws_bytes,
                   void* stream);
+
+/* h3_modulation for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and outputs, with its scratch (the time embedder's hidden
+ * and conditioning vectors, 6 x hidden fp32) in a static device array of the
+ * library, 6 x 8192 floats (192 KiB) per GPU, held until the process ends.
+ * No workspace argument; the call allocates nothing.  hidden above 8192:
+ * H3_EUNSUPPORTED.  Every call on one GPU shares that array, so calls that
+ * overlap on one GPU (concurrent streams or threads) race; serialize them.
+ * Other errors as h3_modulation. */
+int h3_modulation_noalloc(const h3_shape* shape, int32_t n_blocks, const h3_time_weights* tw,
+                          const float* sigma3, float* mod, float* mod_final, void* stream);
 
 /* The denoising loop on the device (h3.c README: Euler transitions, video and
  * audio on independent schedules, a terminal zero after the last pass).  For

@@ -317,3 +317,23 @@ def test_binding_refuses_wrong_tensors_before_any_call():
                                   vv, va, ws), "mod: ")
     refused(lambda: B.dit_forward(shape, ts, [w], head, mod, f32(6 * H), rope, x,
                                   vv, f32(3), ws), "vel_audio: ")
+
+
+def test_noalloc_modulation_validates_before_touching_the_gpu(lib):
+    """h3_modulation_noalloc refuses a hidden width beyond its static array
+    (6 x 8192 floats) and missing arguments on the host, before it looks up
+    the array on a device (this runs without a GPU)."""
+    shape, ts = _shape(S.TINY)
+    tw = B.H3TimeWeights()
+    sig = (ctypes.c_float * 3)(1, 1, 1)
+    big = B.H3Shape.from_buffer_copy(shape)
+    big.hidden = 8448
+    rc = lib.h3_modulation_noalloc(ctypes.byref(big), 1, ctypes.byref(tw), sig, None, None, None)
+    assert rc == B.H3_EUNSUPPORTED and "static scratch" in B.last_error()
+    rc = lib.h3_modulation_noalloc(None, 1, ctypes.byref(tw), sig, None, None, None)
+    assert rc == B.H3_EINVAL
+    rc = lib.h3_modulation_noalloc(ctypes.byref(shape), 1, ctypes.byref(tw), None, None, None,
+                                   None)
+    assert rc == B.H3_EINVAL and "sigma3" in B.last_error()
+    rc = lib.h3_modulation_noalloc(ctypes.byref(shape), 1, ctypes.byref(tw), sig, None, None, None)
+    assert rc == B.H3_EINVAL and "time weights" in B.last_error()
