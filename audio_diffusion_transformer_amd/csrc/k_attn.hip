@@ -53,6 +53,13 @@ __device__ __forceinline__ bf16x8_t pack8(const float* p) {
   return as_bf16x8(w);
 }
 
+// max(a, b), NaN if either is NaN (IEEE 754-2019 maximum): gfx950 has it as
+// one instruction (v_maximum3_f32), where fmaxf needs each operand quieted
+// first.  A NaN score makes its query's output NaN either way.
+__device__ __forceinline__ float fmax_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // The value of lanes l ^ 16 (and l ^ 32) through the gfx950 lane-swap
 // instructions: with both operands equal, v_permlane16_swap returns rows
 // (r0, r0, r2, r2) and (r1, r1, r3, r3) of 16 lanes, v_permlane32_swap
@@ -60,11 +67,11 @@ __device__ __forceinline__ bf16x8_t pack8(const float* p) {
 // reduction, computed in the same operand order in every lane.
 __device__ __forceinline__ float max_x16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_x32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_x16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -125,7 +132,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   uint8_t* const sValid = reinterpret_cast<uint8_t*>(sList + a.max_list);     // [n_chunks]
   bf16_t* const ring = reinterpret_cast<bf16_t*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in SGPRs
   // Work order.  Dense query blocks first (they are the long ones), then video
   // blocks.  Workgroup ids are dealt round-robin over the 8 XCDs; when the head
   // count is a multiple of 8, head h is given to XCD h % 8 (XCD x runs the
@@ -286,11 +294,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(
       lds_addr(ring + part * CH + sub * (NDMA * 64 * 8)));
   auto issue = [&](int stage, int chunk) {
-    const uint64_t sa = (uint64_t)(uintptr_t)(gsrc + (size_t)chunk * cstride);
-    // (the builtin returns int: widen through uint32_t, never by sign extension)
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sa);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sa >> 32));
-    const void* src = (const void*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+    // (the chunk id is wave-uniform: the address is formed in SGPRs)
+    const int cs = __builtin_amdgcn_readfirstlane(chunk);
+    const void* src = gsrc + (size_t)(uint32_t)cs * cstride;
     const uint32_t dst = lds0 + (uint32_t)(stage * STG * 2);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) dma16(src, goff[i], dst + i * 1024);
@@ -348,9 +354,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     float mloc = sv[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, sv[e]);
+    for (int e = 1; e < 8; ++e) mloc = fmax_nan(mloc, sv[e]);
     mloc = max_x32(max_x16(mloc));
-    const float m_new = fmaxf(m, mloc);
+    const float m_new = fmax_nan(m, mloc);
     if (__any(m_new > m)) {
       const float alpha = __builtin_amdgcn_exp2f((m - m_new) * sl2);  // 0 on the first chunk
       l *= alpha;
