@@ -68,7 +68,7 @@ struct HeadsArgs {
   const float* rope;     // [R][d/2][2] or null (MODE_QKV)
   bf16_t* q;             // [nh][Rp][d]
   bf16_t* k;             // [nh][Rp][d]
-  bf16_t* vt;            // [nh][d][Rp]
+  bf16_t* vt;            // [nh][Rp/32][d][32]
   float* qbar;           // [nh][nQ][d]
   float* kbar;           // [nh][nT][d]
   float* vbar;           // [nh][nT][d]
@@ -99,7 +99,7 @@ hipError_t launch_route(int head_dim, const RouteArgs& a, hipStream_t s);
 struct AttnArgs {
   const bf16_t* q;          // [nh][Rp][d]
   const bf16_t* k;          // [nh][Rp][d]
-  const bf16_t* vt;         // [nh][d][Rp]
+  const bf16_t* vt;         // [nh][Rp/32][d][32]
   const int* sel;           // [nh][nQ][nsel]
   const float* scores;      // [nh][nQ][nT]: the tile scores (visiting order of the tiles)
   const float* pooled;      // [nh][nQ][d] or null

@@ -11,9 +11,10 @@
 // the bf16 rounding; a text or audio row attends every row.
 //
 // Operands (written by the head-layout kernel): q, k [nh][Rp][D] and v^T
-// [nh][D][Rp] in a padded row space where every tile starts on a multiple of
-// 32 rows; a 32-row "chunk" therefore never straddles two tiles, and
-// chunk_valid[c] gives its number of real rows.
+// blocked per 32-row chunk, [nh][Rp/32][D][32], in a padded row space where
+// every tile starts on a multiple of 32 rows; a 32-row "chunk" therefore never
+// straddles two tiles, its K rows and its v^T block are each 32 x D contiguous
+// bf16, and chunk_valid[c] gives its number of real rows.
 //
 // One workgroup (4 wave64) per (64-row query block, head); wave w owns the 16
 // queries 16w .. 16w+15 of the block, and all four waves walk the block's key
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // swizzle is applied to the global side.
   const int part = wave >> 1, sub = wave & 1;
   const bf16_t* const gsrc = part == 0 ? a.k + (size_t)h * Rp * D : a.vt + (size_t)h * D * Rp;
-  const size_t cstride = part == 0 ? (size_t)32 * D : (size_t)32;
+  const size_t cstride = (size_t)32 * D;  // a K chunk and a v^T chunk are both 32 x D, contiguous
   uint32_t goff[NDMA];  // byte offsets of this lane's 16-byte units within a chunk
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       goff[i] = 2u * (uint32_t)(row * D + (((p % U) ^ swz_k<D>(row)) * 8));
     } else {
       const int d = p >> 2;
-      goff[i] = 2u * ((uint32_t)d * (uint32_t)a.Rp + (uint32_t)(((p & 3) ^ swz_v(d)) * 8));
+      goff[i] = 2u * ((uint32_t)d * 32u + (uint32_t)(((p & 3) ^ swz_v(d)) * 8));
     }
   }
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(

@@ -14,9 +14,10 @@
 //   u~ = bf( rope( u * (sum u^2 / D + eps)^-1/2 * gain ) )
 //   rope: (a, b) -> (a cos - b sin, b cos + a sin) on the pairs (i, i + D/2),
 //   cos/sin from the caller's table; the partner element sits D/16 lanes away.
-// v rows are staged in LDS and written transposed (v^T [nh][D][Rp]) in
-// 16-byte runs of 8 positions; within each aligned 32-row group the 4-row
-// blocks are interleaved (see below).  Padded rows (beyond a tile's
+// v rows are staged in LDS and written transposed, one 32-row chunk at a
+// time (v^T [nh][Rp/32][D][32]: the D x 32 block of a chunk is 8 KB of
+// contiguous memory), in 16-byte runs of 8 positions; within each chunk the
+// 4-row blocks are interleaved (see below).  Padded rows (beyond a tile's
 // length, up to the next multiple of 32) are written as zeros.  Tile sums of
 // q~, k~ and v are kept in fp32 per lane, combined across lanes and waves in
 // a fixed order, and divided by the tile's true row count.
@@ -192,7 +193,8 @@ __global__ __launch_bounds__(256) void k_heads(HeadsArgs a) {
       w[1] = (uint32_t)sV[(r0 + 2) * SV + d] | ((uint32_t)sV[(r0 + 3) * SV + d] << 16);
       w[2] = (uint32_t)sV[(r1 + 0) * SV + d] | ((uint32_t)sV[(r1 + 1) * SV + d] << 16);
       w[3] = (uint32_t)sV[(r1 + 2) * SV + d] | ((uint32_t)sV[(r1 + 3) * SV + d] << 16);
-      *reinterpret_cast<u32x4_t*>(a.vt + ((size_t)h * D + d) * a.Rp + ps + c0 + 8 * p8) = w;
+      const size_t chunk = ((size_t)h * a.Rp + ps + c0) >> 5;  // ps + c0: a multiple of 32
+      *reinterpret_cast<u32x4_t*>(a.vt + (chunk * D + d) * 32 + 8 * p8) = w;
     }
     __syncthreads();
   }

@@ -124,7 +124,8 @@ typedef struct {
  * diagnostics).  After h3_block_forward returns (and the stream is synced)
  * the workspace holds: n2 (the MLP norm output, [R][H] bf16, in `norm`),
  * the GELU activations ([R][F] bf16, in `big`), the head-major padded
- * q, k ([nh][Rp][d] bf16) and v transposed ([nh][d][Rp] bf16), the tile
+ * q, k ([nh][Rp][d] bf16) and v transposed per 32-row chunk ([nh][Rp/32][d][32]
+ * bf16, the 4-row blocks of a chunk in the order 0, 4, 1, 5, 2, 6, 3, 7), the tile
  * means (fp32 [nh][nQ][d], [nh][n_tiles][d] x2), scores (fp32
  * [nh][nQ][n_tiles]), sel (int32 [nh][nQ][min(top_k, nQ)]), pooled (fp32
  * [nh][nQ][d]), attn ([R][H] bf16) and x1 ([R][H] bf16).  Padded row space:

@@ -56,7 +56,8 @@ class BlockRun:
         r = {}
         r["q"] = P.unpad_rows(b2f(view(lay.q, np.uint16, (nh, Rp, d))), ts, tp)
         r["k"] = P.unpad_rows(b2f(view(lay.k, np.uint16, (nh, Rp, d))), ts, tp)
-        vt_bits = vt_key_order(view(lay.vt, np.uint16, (nh, d, Rp)))
+        vt_blk = view(lay.vt, np.uint16, (nh, Rp // 32, d, 32))     # per 32-row chunk
+        vt_bits = vt_key_order(np.swapaxes(vt_blk, 1, 2).reshape(nh, d, Rp))
         vt = b2f(vt_bits)
         r["v"] = P.unpad_rows(np.swapaxes(vt, 1, 2), ts, tp)
         r["q_pad"] = view(lay.q, np.uint16, (nh, Rp, d))
