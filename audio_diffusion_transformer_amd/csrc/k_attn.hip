@@ -37,6 +37,8 @@
 // V^T row are one 16-byte run.  The probabilities never leave their lanes;
 // the four lanes that share a query exchange the running max with two
 // shuffles.  Scores are scaled into the log2 domain (exp2).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -309,8 +311,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __builtin_amdgcn_s_waitcnt(0);  // q fragments in registers before the chunk stream starts
   int chunk = nchunk > 0 ? chunk_at(0) : 0;
   if (nchunk > 0) issue(0, chunk);
-  for (int ci = 0; ci < nchunk; ++ci) {
-    const int cur = ci & 1;
+  // (the step is written once for each ring stage, so that the stage's LDS
+  // addresses are constants of the unrolled loop)
+  auto step = [&](const int ci, auto stage) {
+    constexpr int cur = decltype(stage)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int this_chunk = chunk;
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       chunk = chunk_at(ci + 1);
       issue(cur ^ 1, chunk);
     }
-    if (!q_live) continue;  // no real query in this wave: loads and barriers only
+    if (!q_live) return;  // no real query in this wave: loads and barriers only
     const int valid = sValid[this_chunk];
     const bf16_t* kb = ring + cur * STG;
     const bf16_t* vb = kb + CH;
@@ -379,7 +383,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           *reinterpret_cast<const u32x4_t*>(vb + d * 32 + ((g ^ swz_v(d)) * 8)));
       o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, p8, o[b], 0, 0, 0);
     }
+  };
+  int ci = 0;
+  for (; ci + 1 < nchunk; ci += 2) {
+    step(ci, std::integral_constant<int, 0>{});
+    step(ci + 1, std::integral_constant<int, 1>{});
   }
+  if (ci < nchunk) step(ci, std::integral_constant<int, 0>{});
   // each lane summed its own 8 keys of a chunk; the query's other keys are in
   // lanes l ^ 16, l ^ 32 and l ^ 48 (the same sum in every one of the four)
   l = sum_x32(sum_x16(l));
