@@ -111,49 +111,35 @@ __global__ __launch_bounds__(256) void k_rows_in(RowsInArgs a) {
 
 // ---- time conditioning: out[s][o] = W[o] . act(in[s]) + b[o], s < 3 --------
 
-constexpr int kTvWaves = 8, kTvRowsPerWave = 8;
+constexpr int kTvWaves = 8;
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
-// dot products of weight row `wr` (bf16, K) with the three staged inputs; the
-// lane takes the 16-byte units lane, lane + 64, ...
-__device__ __forceinline__ void dot3(const bf16_t* __restrict__ wr, const float* sIn, int K,
-                                     int lane, float& a0, float& a1, float& a2) {
-  for (int k8 = lane * 8; k8 < K; k8 += 512) {
-    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(wr + k8);
-    float wf[8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      wf[2 * t] = bflo(wv[t]);
-      wf[2 * t + 1] = bfhi(wv[t]);
-    }
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const f32x4_t i0 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8]);
-      const f32x4_t i1 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8 + 4]);
-      float acc = s == 0 ? a0 : (s == 1 ? a1 : a2);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc = fmaf(wf[t], i0[t], acc);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc = fmaf(wf[4 + t], i1[t], acc);
-      if (s == 0) a0 = acc; else if (s == 1) a1 = acc; else a2 = acc;
-    }
-  }
-}
-
+// One wave: RW weight rows against the three staged inputs at once (eight for
+// the large products, two for the small ones so that they still give every CU
+// work), so that each lane keeps RW 16-byte weight loads in flight and reads
+// each staged input value once for all of its rows.  The lane takes the
+// 16-byte units lane, lane + 64, ... of a row and sums them in that order; the
+// 64 lane sums are then added by wave_sum.
+template <int RW>
 __global__ __launch_bounds__(64 * kTvWaves) void k_time_gemv(TimeGemvArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float sIn[];  // [3][K]
+  extern __shared__ __attribute__((aligned(16))) float sIn[];  // [3][K], then the outputs [3][ROWS]
+  constexpr int ROWS = kTvWaves * RW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K;
   if (a.in == nullptr) {
     // the frequency embedding of t_s = 1000 sigma_s (fp64 arguments, so the
-    // large angles keep their accuracy)
-    for (int idx = tid; idx < 3 * K; idx += 64 * kTvWaves) {
-      const int s = idx / K, i = idx % K, half = K / 2;
-      const int f = i < half ? i : i - half;
+    // large angles keep their accuracy): cos in [0, K/2), sin in [K/2, K)
+    const int half = K / 2;
+    for (int f = tid; f < half; f += 64 * kTvWaves) {
       const double om = exp(-9.210340371976184 * (double)f / (double)half);  // 10000^(-f/half)
-      const double ang = 1000.0 * (double)a.sigma[s] * om;
-      sIn[idx] = (float)(i < half ? cos(ang) : sin(ang));
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        double sn, cs;
+        sincos(1000.0 * (double)a.sigma[s] * om, &sn, &cs);
+        sIn[s * K + f] = (float)cs;
+        sIn[s * K + half + f] = (float)sn;
+      }
     }
   } else {
     for (int idx = 4 * tid; idx < 3 * K; idx += 4 * 64 * kTvWaves) {
@@ -165,31 +151,74 @@ __global__ __launch_bounds__(64 * kTvWaves) void k_time_gemv(TimeGemvArgs a) {
     }
   }
   __syncthreads();
-  const int o0 = (blockIdx.x * kTvWaves + wave) * kTvRowsPerWave;
-  for (int rr = 0; rr < kTvRowsPerWave; rr += 2) {
-    const int o = o0 + rr;
-    if (o >= a.N) break;  // uniform over the wave
-    const bool two = o + 1 < a.N;
-    float x0 = 0.f, x1 = 0.f, x2 = 0.f, y0 = 0.f, y1 = 0.f, y2 = 0.f;
-    dot3(a.w + (size_t)o * K, sIn, K, lane, x0, x1, x2);
-    if (two) dot3(a.w + (size_t)(o + 1) * K, sIn, K, lane, y0, y1, y2);
-    x0 = wave_sum(x0); x1 = wave_sum(x1); x2 = wave_sum(x2);
-    y0 = wave_sum(y0); y1 = wave_sum(y1); y2 = wave_sum(y2);
+  const int ob = blockIdx.x * ROWS;            // the workgroup's first output
+  const int o0 = ob + wave * RW;               // this wave's first row
+  float acc[RW][3];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int oo = o + q;
-      if (lane < 3 && (q == 0 || two)) {
-        const float sum = q == 0 ? (lane == 0 ? x0 : (lane == 1 ? x1 : x2))
-                                 : (lane == 0 ? y0 : (lane == 1 ? y1 : y2));
-        float v = sum + bf2f(a.b[oo]);
-        if (a.out_silu) v = silu_f(v);
-        if (a.table == nullptr) {
-          a.out[(size_t)lane * a.N + oo] = v;
-        } else {  // modulation tables: mod[l][s][o] = v + table[l][o]
-          for (int l = 0; l < a.n_blocks; ++l)
-            a.out[((size_t)l * 3 + lane) * a.N + oo] = v + bf2f(a.table[(size_t)l * a.N + oo]);
+  for (int r = 0; r < RW; ++r) acc[r][0] = acc[r][1] = acc[r][2] = 0.f;
+  for (int k8 = lane * 8; k8 < K; k8 += 512) {
+    u32x4_t wv[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int o = min(o0 + r, a.N - 1);      // rows past N: a valid row, result dropped
+      wv[r] = *reinterpret_cast<const u32x4_t*>(a.w + (size_t)o * K + k8);
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      const f32x4_t i0 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8]);
+      const f32x4_t i1 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8 + 4]);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        float v = acc[r][s];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          v = fmaf(bflo(wv[r][t]), i0[2 * t], v);
+          v = fmaf(bfhi(wv[r][t]), i0[2 * t + 1], v);
         }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          v = fmaf(bflo(wv[r][2 + t]), i1[2 * t], v);
+          v = fmaf(bfhi(wv[r][2 + t]), i1[2 * t + 1], v);
+        }
+        acc[r][s] = v;
       }
+    }
+  }
+  __syncthreads();  // every wave is done with the staged inputs
+  float* const sOut = sIn;  // [3][ROWS]
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      const float v = wave_sum(acc[r][s]);
+      if (lane == 0) sOut[s * ROWS + wave * RW + r] = v;
+    }
+  __syncthreads();
+  // bias, activation and the stores, one output per lane (coalesced rows of
+  // ROWS outputs): out[s][o], or the modulation tables out[l][s][o] = v + table[l][o].
+  // Eight table reads are issued before their eight stores.
+  const int nl = a.table == nullptr ? 1 : a.n_blocks;
+  const int total = nl * 3 * ROWS;
+  constexpr int NB = 8, STRIDE = 64 * kTvWaves;
+  for (int base = tid; base < total; base += NB * STRIDE) {
+    float tv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int idx = base + u * STRIDE;
+      const int j = idx % ROWS, l = idx / (3 * ROWS);
+      tv[u] = 0.f;
+      if (a.table != nullptr && idx < total && ob + j < a.N)
+        tv[u] = bf2f(a.table[(size_t)l * a.N + ob + j]);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int idx = base + u * STRIDE;
+      const int j = idx % ROWS, ls = idx / ROWS, s = ls % 3, l = ls / 3;
+      const int o = ob + j;
+      if (idx >= total || o >= a.N) continue;
+      float v = sOut[s * ROWS + j] + bf2f(a.b[o]);
+      if (a.out_silu) v = silu_f(v);
+      a.out[((size_t)l * 3 + s) * a.N + o] = v + tv[u];
     }
   }
 }
@@ -325,10 +354,13 @@ hipError_t launch_rows_in(const RowsInArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_time_gemv(const TimeGemvArgs& a, hipStream_t s) {
-  const int rows_per_wg = kTvWaves * kTvRowsPerWave;
+  // eight rows a wave from N = 8,192 on (at least 128 workgroups); below, two
+  const bool big = a.N >= 8192;
+  const int rows_per_wg = kTvWaves * (big ? 8 : 2);
   dim3 grid((a.N + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL(k_time_gemv, grid, dim3(64 * kTvWaves), (size_t)3 * a.K * sizeof(float), s,
-                     a);
+  const size_t lds = (size_t)3 * (a.K > rows_per_wg ? a.K : rows_per_wg) * sizeof(float);
+  if (big) hipLaunchKernelGGL(k_time_gemv<8>, grid, dim3(64 * kTvWaves), lds, s, a);
+  else hipLaunchKernelGGL(k_time_gemv<2>, grid, dim3(64 * kTvWaves), lds, s, a);
   return hipGetLastError();
 }
 
