@@ -93,6 +93,10 @@ def test_topk_nan_scores_rank_last():
     # the pooled branch of head 0 is NaN for every video tile (as in the oracle)
     vid = slice(sh.n_prefix, sh.rows)
     assert np.array_equal(np.isnan(g["out"][vid, :64]), np.isnan(r["out"][vid, :64]))
+    # the text and audio rows of head 0 attend the NaN key itself: NaN, as in the oracle
+    pre = slice(0, sh.n_prefix)
+    assert np.isnan(r["out"][pre, :64]).all()
+    assert np.array_equal(np.isnan(g["out"][pre, :64]), np.isnan(r["out"][pre, :64]))
     assert not np.isnan(g["out"][:, 64:]).any()
 
 
