@@ -6,11 +6,15 @@
 // 32 -> 5376 audio patch projections keep F32 weights, inputs and
 // accumulation and round each result straight into the packed hidden
 // stream); TensorFold PR #949, "What it adds" (the rows in).
-//   x[row][c] = bf( sum_k patch[row][k] W[c][k] + b[c] )   fp32, k ascending
-// One workgroup per 64 rows x 256 columns of one segment: 32-wide k slices
-// of W and of the patches are staged in LDS (both k-major); each thread owns
-// 8 rows x 8 consecutive columns and writes them as 16-byte bf16 runs.  Text
-// rows (the text encoder's output) are copied as they are.
+//   x[row][c] = bf( sum_k patch[row][k] W[c][k] + b[c] )   fp32 products and sums
+// One workgroup (4 waves) per 64 rows x 256 columns of one segment: 32-wide k
+// slices of W and of the patches are staged in LDS (row-major, k contiguous);
+// wave w computes the 64 x 64 block of columns 64w .. 64w+63 with fp32 matrix
+// products (v_mfma_f32_16x16x4_f32, fp32 accumulation; lane group g feeds the
+// products' k slot g with k = 4g .. 4g+3 of each 16-wide half slice, so one
+// 16-byte LDS read serves four products); the sums plus bias are rounded to
+// bf16, staged in LDS and written as 16-byte runs.  Text rows (the text
+// encoder's output) are copied as they are.
 //
 // Time conditioning: TensorFold PR #949, "What comes next" (the time embedder
 // and the modulation tables).  For each segment s (text, audio, video) with
@@ -60,52 +64,76 @@ __global__ __launch_bounds__(256) void k_rows_in(RowsInArgs a) {
   const float* __restrict__ bias = seg == 1 ? a.b_audio : a.b_video;
   const int C = seg == 1 ? a.c_audio : a.c_video;
 
-  __shared__ __attribute__((aligned(16))) float sW[kRiK][kRiCols + 4];  // [k][column]
-  __shared__ __attribute__((aligned(16))) float sP[kRiK][kRiRows + 4];  // [k][row]
-  const int cg = tid & 31, rg = tid >> 5;  // columns 8 cg .. 8 cg + 7; rows 8 rg .. 8 rg + 7
-  float acc[8][8];
+  constexpr int SK = kRiK + 4;  // padded row of a staged k slice (16-byte reads free of conflicts)
+  constexpr int SO = kRiCols + 8;  // padded bf16 row of the output staging
+  __shared__ __attribute__((aligned(16))) float sW[kRiCols * SK];  // [column][k]
+  __shared__ __attribute__((aligned(16))) float sP[kRiRows * SK];  // [row][k]
+  static_assert(kRiRows * SO * 2 <= kRiCols * SK * 4, "output staging fits sW");
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  f32x4_t acc[4][4];  // blocks (row block i, column block j) of the wave's 64 x 64
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // a thread's share of a k slice: 32 W values and 8 patch values, all
+  // loaded before any is stored, so that their latencies overlap
+  constexpr int NW = kRiCols * kRiK / 256, NP = kRiRows * kRiK / 256;
+  const int kt = tid % kRiK, ct = tid / kRiK;  // k of this thread; its first column (row)
   for (int k0 = 0; k0 < C; k0 += kRiK) {
-    __syncthreads();
-    for (int idx = tid; idx < kRiCols * kRiK; idx += 256) {
-      const int c = idx / kRiK, k = idx % kRiK;
-      sW[k][c] = k0 + k < C ? W[(size_t)(n0 + c) * C + k0 + k] : 0.f;
-    }
-    for (int idx = tid; idx < kRiRows * kRiK; idx += 256) {
-      const int r = idx / kRiK, k = idx % kRiK;
-      sP[k][r] = (m0 + r < nrows && k0 + k < C) ? patch[(size_t)(m0 + r) * C + k0 + k] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 2
-    for (int k = 0; k < kRiK; ++k) {
-      const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(&sW[k][8 * cg]);
-      const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(&sW[k][8 * cg + 4]);
-      const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(&sP[k][8 * rg]);
-      const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(&sP[k][8 * rg + 4]);
-      const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-      const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    float wv[NW], pv[NP];
+    const bool kin = k0 + kt < C;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+    for (int u = 0; u < NW; ++u) {
+      const int c = ct + u * (256 / kRiK);
+      wv[u] = kin ? W[(size_t)(n0 + c) * C + k0 + kt] : 0.f;
+    }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(pv[i], wv[j], acc[i][j]);
+    for (int u = 0; u < NP; ++u) {
+      const int r = ct + u * (256 / kRiK);
+      pv[u] = (kin && m0 + r < nrows) ? patch[(size_t)(m0 + r) * C + k0 + kt] : 0.f;
+    }
+    __syncthreads();  // every wave is done with the previous slice
+#pragma unroll
+    for (int u = 0; u < NW; ++u) sW[(ct + u * (256 / kRiK)) * SK + kt] = wv[u];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) sP[(ct + u * (256 / kRiK)) * SK + kt] = pv[u];
+    __syncthreads();
+#pragma unroll
+    for (int hk = 0; hk < kRiK; hk += 16) {  // two 16-wide halves of the slice
+      const int kk = hk + 4 * g;
+      f32x4_t pa[4], wb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pa[i] = *reinterpret_cast<const f32x4_t*>(&sP[(16 * i + l16) * SK + kk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wb[j] = *reinterpret_cast<const f32x4_t*>(&sW[(64 * wave + 16 * j + l16) * SK + kk]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[i][t], wb[j][t], acc[i][j], 0, 0, 0);
     }
   }
-  const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(bias + n0 + 8 * cg);
-  const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(bias + n0 + 8 * cg + 4);
+  // bias, bf16, staged row-major (lane: rows 16i + 4g + e, column 64 wave + 16j + l16)
+  __syncthreads();  // every wave is done with the k slices
+  bf16_t* const sO = reinterpret_cast<bf16_t*>(sW);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * rg + i;
-    if (m0 + r >= nrows) continue;
-    u32x4_t w;
+  for (int j = 0; j < 4; ++j) {
+    const int col = 64 * wave + 16 * j + l16;
+    const float bv = bias[n0 + col];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      w[t] = pack2(acc[i][2 * t] + b0[2 * t], acc[i][2 * t + 1] + b0[2 * t + 1]);
-      w[2 + t] = pack2(acc[i][4 + 2 * t] + b1[2 * t], acc[i][4 + 2 * t + 1] + b1[2 * t + 1]);
-    }
-    *reinterpret_cast<u32x4_t*>(a.x + (size_t)(row0 + m0 + r) * H + n0 + 8 * cg) = w;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sO[(16 * i + 4 * g + e) * SO + col] = f2bf(acc[i][j][e] + bv);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kRiRows * (kRiCols / 8); idx += 256) {
+    const int r = idx / (kRiCols / 8), c8 = (idx % (kRiCols / 8)) * 8;
+    if (m0 + r < nrows)
+      *reinterpret_cast<u32x4_t*>(a.x + (size_t)(row0 + m0 + r) * H + n0 + c8) =
+          *reinterpret_cast<const u32x4_t*>(&sO[r * SO + c8]);
   }
 }
 
