@@ -16,6 +16,7 @@
 // lifetimes: one [R][H] buffer holds n1 then n2, one [R][max(3H, F)] buffer
 // holds the QKV output then the MLP activations.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 
 #include <mutex>
@@ -45,6 +46,18 @@ int fail(int code, const char* fmt, ...) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Guard bands, a debugging aid: with H3_WS_GUARD=<n> in the environment every
+// region of a workspace is followed by n bytes (rounded up to 256) that no
+// kernel touches, so a caller that fills the workspace with a pattern can
+// find a stray write past a region as a changed band.  Unset, or 0: regions
+// are packed.  Read at every planning call.
+size_t ws_guard() {
+  const char* e = getenv("H3_WS_GUARD");
+  if (e == nullptr) return 0;
+  const long v = strtol(e, nullptr, 10);
+  return v > 0 && v <= (1l << 24) ? align256((size_t)v) : 0;
+}
 
 struct Plan {
   h3_shape s;
@@ -164,9 +177,10 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
   h3_ws_layout& L = p.lay;
   L = h3_ws_layout{};
   size_t off = 0;
+  const size_t guard = ws_guard();
   auto take = [&](size_t bytes) {
     const size_t o = off;
-    off = align256(off + bytes);
+    off = align256(off + bytes) + guard;
     return o;
   };
   const size_t bf = 2, f4 = 4;
@@ -667,9 +681,10 @@ struct DenoiseLayout {
 DenoiseLayout denoise_layout(const Plan& p, int n_blocks) {
   DenoiseLayout d{};
   size_t off = p.lay.total;
+  const size_t guard = ws_guard();
   auto take = [&](size_t bytes) {
     const size_t o = off;
-    off = align256(off + bytes);
+    off = align256(off + bytes) + guard;
     return o;
   };
   d.x = take((size_t)p.R * p.H * 2);
@@ -691,9 +706,10 @@ struct TrLayout {
 TrLayout tr_layout(const Plan& pf, const Plan& pr) {
   TrLayout t{};
   size_t off = align256(pf.lay.total > pr.lay.total ? pf.lay.total : pr.lay.total);
+  const size_t guard = ws_guard();
   auto take = [&](size_t bytes) {
     const size_t o = off;
-    off = align256(off + bytes);
+    off = align256(off + bytes) + guard;
     return o;
   };
   t.orig = take((size_t)(pf.s.n_video > 0 ? pf.s.n_video : 1) * pf.H * 2);

@@ -147,7 +147,14 @@ int h3_abi_version(void);
 const char* h3_last_error(void);
 
 /* Bytes of workspace needed by the entry point `which` (H3_WS_*) for this
- * shape and tile map; 0 on invalid input (see h3_last_error). */
+ * shape and tile map; 0 on invalid input (see h3_last_error).
+ * Debugging aid: with the environment variable H3_WS_GUARD=<n> set at
+ * planning time, every workspace region (of these calls and of
+ * h3_denoise_workspace_bytes / the token-reduction forward) is followed by n
+ * bytes, rounded up to 256, that no kernel touches; the sizes and offsets
+ * reported here include the bands.  A caller can fill the workspace with a
+ * pattern and check the bands after a call.  The same variable must be set
+ * when the workspace is sized and when the call runs. */
 size_t h3_workspace_bytes(const h3_shape* shape, const int32_t* tile_start, int32_t which);
 
 /* Offsets of the workspace regions (see h3_ws_layout).  Returns H3_OK or an error. */

@@ -337,3 +337,19 @@ def test_noalloc_modulation_validates_before_touching_the_gpu(lib):
     assert rc == B.H3_EINVAL and "sigma3" in B.last_error()
     rc = lib.h3_modulation_noalloc(ctypes.byref(shape), 1, ctypes.byref(tw), sig, None, None, None)
     assert rc == B.H3_EINVAL and "time weights" in B.last_error()
+
+
+def test_guard_bands_grow_the_plan():
+    """CPU-side: the bands add (regions x band) bytes and keep every offset
+    256-byte aligned; unset, the plan is the packed one."""
+    from guard_bands import GUARD, guard_bands, region_starts
+    sh = S.TINY
+    ts, npt = S.tile_map(sh)
+    shape = B.make_shape(sh, ts, npt)
+    with guard_bands(0):
+        plain = B.workspace_layout(shape, ts, B.H3_WS_DIT)
+    with guard_bands(GUARD):
+        banded = B.workspace_layout(shape, ts, B.H3_WS_DIT)
+    starts = region_starts(banded, ts)
+    assert all(s % 256 == 0 for s in starts)
+    assert banded.total == plain.total + (len(starts) + 1) * GUARD
