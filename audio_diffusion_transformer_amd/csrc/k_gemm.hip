@@ -100,21 +100,22 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// GELU z * Phi(z), Phi(z) = (1 + erf(z / sqrt2)) / 2, with erfc(x), x >= 0, from
-// Abramowitz & Stegun 7.1.26: erfc(x) = (a1 t + ... + a5 t^5) e^(-x^2),
-// t = 1 / (1 + p x), |error| <= 1.5e-7.  Phi(z) = 1 - erfc(x)/2 for z >= 0 and
-// erfc(x)/2 for z < 0 (x = |z| / sqrt2), so the negative tail is computed
-// without cancellation.  Straight-line code: one reciprocal, one exp2.
+// GELU z * Phi(z), Phi(z) = (1 + erf(z / sqrt2)) / 2, with erfc(x), x = |z| / sqrt2,
+// from Abramowitz & Stegun 7.1.26: erfc(x) = (a1 t + ... + a5 t^5) e^(-x^2),
+// t = 1 / (1 + p x), |error| <= 1.5e-7.  With q = erfc(x) / 2 (the
+// coefficients halved), z Phi(z) = max(z, 0) - |z| q for either sign of z
+// (z >= 0: z (1 - q); z < 0: z q): one fused multiply-add at the end, and the
+// negative tail is computed without cancellation.  Straight-line code: one
+// reciprocal, one exp2.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float p = fmaf(1.061405429f, t, -1.453152027f);
-  p = fmaf(p, t, 1.421413741f);
-  p = fmaf(p, t, -0.284496736f);
-  p = fmaf(p, t, 0.254829592f);
-  const float q = p * t * __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);  // erfc(x)
-  const float phi = z >= 0.f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
-  return z * phi;
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164190f, az, 1.0f));  // p / sqrt2
+  float q = fmaf(0.5307027145f, t, -0.7265760135f);                   // a5 / 2, a4 / 2
+  q = fmaf(q, t, 0.7107068705f);                                       // a3 / 2
+  q = fmaf(q, t, -0.142248368f);                                       // a2 / 2
+  q = fmaf(q, t, 0.127414796f);                                        // a1 / 2
+  q = q * t * __builtin_amdgcn_exp2f((z * -0.72134752044448170f) * z);  // e^(-z^2 / 2)
+  return fmaf(-az, q, __builtin_elementwise_maximum(z, 0.0f));
 }
 
 __device__ __forceinline__ int seg_of(int row, int n_text, int n_prefix) {
