@@ -4,11 +4,12 @@
 // TensorFold PR #949: "What it adds" (h3_attention: tile-routed attention
 // with fp32 scores and an online softmax), "Precision" (softmax weights
 // rounded to bf16 before the value product) and the parity notes (the audio
-// rows attend densely).  A video row of query tile i attends the prefix rows,
-// then the rows of the selected tiles sel[h][i] in ascending order, and gets
-// the fp32 pooled branch pooled[h][i] (times the routing gate g of the row,
-// when one is given: "What it adds", q/k/v and the routing gate) added before
-// the bf16 rounding; a text or audio row attends every row.
+// rows attend densely).  A video row of query tile i attends the prefix rows
+// and the rows of the selected tiles sel[h][i], and gets the fp32 pooled
+// branch pooled[h][i] (times the routing gate g of the row, when one is
+// given: "What it adds", q/k/v and the routing gate) added before the bf16
+// rounding; a text or audio row attends every row.  (The kernel's visiting
+// order of the keys, below, changes only where the online softmax rounds.)
 //
 // Operands (written by the head-layout kernel): q, k [nh][Rp][D] and v^T
 // blocked per 32-row chunk, [nh][Rp/32][D][32], in a padded row space where
