@@ -24,8 +24,9 @@
 //   mod[l][s] = W_mod silu(c_s) + b_mod + table[l];  final[s] = W_final silu(c_s) + b_final
 // as four matrix-vector products over the three segments at once: a
 // workgroup (8 waves) stages the three input vectors (fp32) in LDS, each wave
-// takes 8 output rows, two at a time, and reads its weight rows once with
-// 16-byte loads (the products are bound by reading the bf16 weights from HBM).
+// takes a few output rows at once (eight for the wide modulation products, two
+// for the narrow ones) and reads its weight rows once with 16-byte loads (the
+// products are bound by reading the bf16 weights from HBM).
 //
 // Euler: h3.c README (Euler transitions; video and audio on independent
 // schedules, a terminal zero after the last pass):
