@@ -42,7 +42,9 @@
 //
 // Epilogues (rounding points of the block; h3.c README on rounded bf16
 // residuals).  The bf16 tile is staged through LDS so that residual loads and
-// output stores are 16-byte coalesced:
+// output stores are 16-byte coalesced.  The outputs are written with
+// nontemporal stores: this kernel never reads them back, and streaming them
+// leaves L2 to the operand panels that the running tiles share.
 //   EPI_BIAS:         C = bf(acc + bias)
 //   EPI_BIAS_GELU:    C = bf(gelu(acc + bias)),  gelu(z) = z/2 (1 + erf(z/sqrt2)) (gelu_erf below)
 //   EPI_BIAS_RESGATE: C = bf(res + gate[seg(row)] * bf(acc + bias))
@@ -377,8 +379,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
       const int row = m0 + wm * 128 + r;
       if (row >= M) continue;
       const int col = (n0 + wn * 64) / 2 + c8;
-      *reinterpret_cast<u32x4_t*>(ep.out + (size_t)row * NO + col) =
-          *reinterpret_cast<const u32x4_t*>(st + r * 32 + c8);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(st + r * 32 + c8),
+                                  reinterpret_cast<u32x4_t*>(ep.out + (size_t)row * NO + col));
     }
     return;
   }
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const void* __restrict__ A
         v[t2] = pack2(fmaf(gv[2 * t2], bflo(v[t2]), bflo(x[t2])),
                       fmaf(gv[2 * t2 + 1], bfhi(v[t2]), bfhi(x[t2])));
     }
-    *reinterpret_cast<u32x4_t*>(ep.out + o) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(ep.out + o));
   }
 }
 

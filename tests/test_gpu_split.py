@@ -47,6 +47,15 @@ def test_split_block_all_stages(mlp, gate, rows):
     _check_block(sh, *_inputs(sh), h_frac=0.1)
 
 
+@pytest.mark.parametrize("mlp", [0, 1])
+def test_block_ragged_last_tile_row(mlp):
+    # 356 rows: the second row of tiles holds 100 rows, so the waves that own
+    # its rows 128-255 compute only clamped copies of row 355, which must
+    # never reach the output
+    sh = WIDE.replace(mlp=mlp, n_video=356 - 64)
+    _check_block(sh, *_inputs(sh), h_frac=0.1)
+
+
 def test_split_block_deterministic():
     """The partial sums are added in a fixed order: two calls give the same bytes."""
     sh = WIDE.replace(mlp=1, gate=1)
