@@ -95,13 +95,13 @@ TRAFFIC = {
     "sources": ["audio_diffusion_transformer_amd/csrc/k_gemm.hip",
                 "audio_diffusion_transformer_amd/csrc/common.h",
                 "audio_diffusion_transformer_amd/csrc/internal.h"],
-    "sources_sha256": "ba467885a11301fc3d5b415ebca7c588e71d62e25d44662cfa0051b0c2a68b39",
+    "sources_sha256": "9d4e0d340313825c6940fd09ed444866ab273d7d8c1bdf5369dbeb9aa9af2665",
     # raw KiB of one FC1 call, its two launches summed (the tiles with the
-    # split last round: 2340445.8958333335 + 32814.5 fetched, 681250.0 + 1686.0 written),
+    # split last round: 2380603.6458333335 + 32814.520833333336 fetched, 681265.0833333334 + 1686.0 written),
     # and the copy's scale factors (1 GiB copy: FETCH_SIZE 524294.5 KiB,
     # WRITE_SIZE 1048576.0 KiB)
-    "fetch_kib": 2373260.3958333335, "fetch_scale": 1.999975,
-    "write_kib": 682936.0, "write_scale": 1.000000,
+    "fetch_kib": 2413418.166666667, "fetch_scale": 1.999975,
+    "write_kib": 682951.0833333334, "write_scale": 1.000000,
 }
 
 
