@@ -185,13 +185,23 @@ __global__ __launch_bounds__(64 * kTvWaves) void k_time_gemv(TimeGemvArgs a) {
   float acc[RW][3];
 #pragma unroll
   for (int r = 0; r < RW; ++r) acc[r][0] = acc[r][1] = acc[r][2] = 0.f;
-  for (int k8 = lane * 8; k8 < K; k8 += 512) {
-    u32x4_t wv[RW];
+  // The next 8 columns' weights are loaded before the current ones are used,
+  // so a load's latency passes under the previous step's products (addresses
+  // clamped into the row, so every load is a valid one; rows past N: a valid
+  // row, result dropped).
+  const bf16_t* wrow[RW];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const int o = min(o0 + r, a.N - 1);      // rows past N: a valid row, result dropped
-      wv[r] = *reinterpret_cast<const u32x4_t*>(a.w + (size_t)o * K + k8);
-    }
+  for (int r = 0; r < RW; ++r) wrow[r] = a.w + (size_t)min(o0 + r, a.N - 1) * K;
+  u32x4_t wv[RW];
+  auto load_w = [&](u32x4_t* dst, int k8) {
+    const int kc = min(k8, K - 8);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) dst[r] = *reinterpret_cast<const u32x4_t*>(wrow[r] + kc);
+  };
+  load_w(wv, lane * 8);
+  for (int k8 = lane * 8; k8 < K; k8 += 512) {
+    u32x4_t wn[RW];
+    load_w(wn, k8 + 512);
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       const f32x4_t i0 = *reinterpret_cast<const f32x4_t*>(&sIn[s * K + k8]);
@@ -212,42 +222,59 @@ __global__ __launch_bounds__(64 * kTvWaves) void k_time_gemv(TimeGemvArgs a) {
         acc[r][s] = v;
       }
     }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) wv[r] = wn[r];
   }
+  // the 3 RW lane sums reduced across the wave together (each the xor tree of
+  // wave_sum, in the same order), so their lane exchanges overlap
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int s = 0; s < 3; ++s) acc[r][s] += __shfl_xor(acc[r][s], o, kWave);
   __syncthreads();  // every wave is done with the staged inputs
   float* const sOut = sIn;  // [3][ROWS]
+  if (lane == 0)
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
+    for (int r = 0; r < RW; ++r)
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const float v = wave_sum(acc[r][s]);
-      if (lane == 0) sOut[s * ROWS + wave * RW + r] = v;
-    }
+      for (int s = 0; s < 3; ++s) sOut[s * ROWS + wave * RW + r] = acc[r][s];
   __syncthreads();
   // bias, activation and the stores, one output per lane (coalesced rows of
   // ROWS outputs): out[s][o], or the modulation tables out[l][s][o] = v + table[l][o].
-  // Eight table reads are issued before their eight stores.
+  // A thread's outputs all share the column j = tid % ROWS (the stride is a
+  // multiple of ROWS), so it reads its bias and three sums once; the table
+  // reads of a group are issued unconditionally (clamped) before its stores.
   const int nl = a.table == nullptr ? 1 : a.n_blocks;
   const int total = nl * 3 * ROWS;
   constexpr int NB = 8, STRIDE = 64 * kTvWaves;
+  static_assert(STRIDE % ROWS == 0, "a thread keeps one output column");
+  const int j = tid % ROWS, o = ob + j;
+  const bool col_ok = o < a.N;
+  const float bias = bf2f(a.b[min(o, a.N - 1)]);
+  const float sv[3] = {sOut[j], sOut[ROWS + j], sOut[2 * ROWS + j]};
+  auto put = [&](int idx, float tv) {
+    const int ls = idx / ROWS, s = ls % 3, l = ls / 3;
+    float v = sv[s] + bias;
+    if (a.out_silu) v = silu_f(v);
+    a.out[((size_t)l * 3 + s) * a.N + o] = v + tv;
+  };
+  if (a.table == nullptr) {
+    for (int idx = tid; idx < total; idx += STRIDE)
+      if (col_ok) put(idx, 0.f);
+    return;
+  }
+  const bf16_t* const tcol = a.table + min(o, a.N - 1);
   for (int base = tid; base < total; base += NB * STRIDE) {
     float tv[NB];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int idx = base + u * STRIDE;
-      const int j = idx % ROWS, l = idx / (3 * ROWS);
-      tv[u] = 0.f;
-      if (a.table != nullptr && idx < total && ob + j < a.N)
-        tv[u] = bf2f(a.table[(size_t)l * a.N + ob + j]);
-    }
+    for (int u = 0; u < NB; ++u)
+      tv[u] = bf2f(tcol[(size_t)min((base + u * STRIDE) / (3 * ROWS), nl - 1) * a.N]);
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int idx = base + u * STRIDE;
-      const int j = idx % ROWS, ls = idx / ROWS, s = ls % 3, l = ls / 3;
-      const int o = ob + j;
-      if (idx >= total || o >= a.N) continue;
-      float v = sOut[s * ROWS + j] + bf2f(a.b[o]);
-      if (a.out_silu) v = silu_f(v);
-      a.out[((size_t)l * 3 + s) * a.N + o] = v + tv[u];
+      if (idx < total && col_ok) put(idx, tv[u]);
     }
   }
 }
