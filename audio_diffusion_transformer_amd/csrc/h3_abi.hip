@@ -47,6 +47,10 @@ int fail(int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Rows of a call: far above any product the GEMMs accept (M K < 2^31), low
+// enough that every row index and padded row count stays an int.
+constexpr int kMaxRows = 1 << 26;
+
 // Guard bands, a debugging aid: with H3_WS_GUARD=<n> in the environment every
 // region of a workspace is followed by n bytes (rounded up to 256) that no
 // kernel touches, so a caller that fills the workspace with a pattern can
@@ -80,6 +84,9 @@ int make_plan(const h3_shape* s, const int32_t* tile_start, int which, Plan& p) 
   p.s = *s;
   if (s->n_text < 0 || s->n_audio < 0 || s->n_video < 0)
     return fail(H3_EINVAL, "negative row count");
+  // (summed in 64 bits: three int32 counts can overflow an int)
+  if ((long long)s->n_text + s->n_audio + s->n_video > kMaxRows)
+    return fail(H3_EUNSUPPORTED, "more than %d rows", kMaxRows);
   p.R = s->n_text + s->n_audio + s->n_video;
   p.P = s->n_text + s->n_audio;
   if (p.R < 1) return fail(H3_EINVAL, "no rows");
@@ -601,6 +608,8 @@ int check_rows_in(const h3_shape* s, const h3_rows_in_weights* w, const h3_bf16*
                   const float* audio, const float* video, const h3_bf16* x) {
   if (!s) return fail(H3_EINVAL, "shape is NULL");
   if (s->n_text < 0 || s->n_audio < 0 || s->n_video < 0) return fail(H3_EINVAL, "negative row count");
+  if ((long long)s->n_text + s->n_audio + s->n_video > kMaxRows)
+    return fail(H3_EUNSUPPORTED, "more than %d rows", kMaxRows);
   if (s->hidden < 256 || s->hidden % 256 != 0 || s->hidden > 8192)
     return fail(H3_EUNSUPPORTED, "hidden %d must be a positive multiple of 256, <= 8192", s->hidden);
   if (!w) return fail(H3_EINVAL, "rows-in weights are required");

@@ -124,6 +124,23 @@ int main(int argc, char** argv) {
       EXPECT(rc != H3_OK, "case %d: routed_attn accepted NULL pointers", c);
     }
   }
+  // row counts whose int32 sum wraps: refused, with no signed overflow on the way
+  {
+    h3_shape s{};
+    s.n_text = 64;
+    s.n_audio = 0x7fffffff;
+    s.n_video = 0x7fffffff;
+    s.hidden = 256;
+    s.n_heads = 4;
+    s.head_dim = 64;
+    s.ffn = 256;
+    s.n_tiles = 1;
+    s.top_k = 1;
+    const int32_t ts[2] = {0, 64};
+    EXPECT(h3_workspace_bytes(&s, ts, H3_WS_BLOCK) == 0, "huge row counts accepted");
+    EXPECT(h3_rows_in(&s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) != H3_OK,
+           "rows_in accepted huge row counts");
+  }
   printf("plan fuzz: %d cases, %d valid plans, %d refused, %d failures\n", n_cases, valid,
          invalid, failures);
   return failures == 0 ? 0 : 1;

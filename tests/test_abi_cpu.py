@@ -117,6 +117,9 @@ def test_workspace_layout_is_consistent(lib):
     (lambda s, t: t.__setitem__(-1, t[-1] + 1), B.H3_EINVAL),
     (lambda s, t: setattr(s, "top_k", 0), B.H3_EINVAL),
     (lambda s, t: setattr(s, "n_text", -1), B.H3_EINVAL),
+    # three row counts whose int32 sum would wrap
+    (lambda s, t: (setattr(s, "n_audio", 2 ** 31 - 1), setattr(s, "n_video", 2 ** 31 - 1)),
+     B.H3_EUNSUPPORTED),
 ])
 def test_invalid_shapes_rejected_on_host(lib, mutate, code):
     shape, ts = _shape(S.TINY)
@@ -188,6 +191,10 @@ def test_denoise_entry_points_validate_before_launch(lib):
     bad.hidden = 300
     rc = lib.h3_rows_in(ctypes.byref(bad), ctypes.byref(rw), None, None, None, None, None)
     assert rc == B.H3_EUNSUPPORTED
+    huge = B.H3Shape.from_buffer_copy(shape)
+    huge.n_audio = huge.n_video = 2 ** 31 - 1  # an int32 sum would wrap
+    rc = lib.h3_rows_in(ctypes.byref(huge), ctypes.byref(rw), None, None, None, None, None)
+    assert rc == B.H3_EUNSUPPORTED and "rows" in B.last_error()
     # modulation: workspace size, missing sigma, missing weights, small workspace
     n = lib.h3_modulation_workspace_bytes(ctypes.byref(shape))
     assert n >= 6 * S.TINY.hidden * 4 and n % 256 == 0
