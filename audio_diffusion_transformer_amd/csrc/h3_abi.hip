@@ -1094,6 +1094,9 @@ int h3_quantize_rows(const h3_bf16* x, int32_t rows, int32_t cols, int32_t group
   if (!quant_shape_ok(cols, G))
     return fail(H3_EINVAL, "cols %d and group %d: multiples of 8, group <= 32768 dividing cols",
                 cols, group);
+  // one wave per (row, group) must fit a launch of at most 2^31 - 1 workgroups of 4 waves
+  if (rows > kMaxRows || (long long)rows * (cols / G) > 4LL * 0x7fffffffLL)
+    return fail(H3_EUNSUPPORTED, "%d rows of %d groups: too many", rows, cols / G);
   if (rows > 0 && (!x || !q || !scale)) return fail(H3_EINVAL, "x, q and scale are required");
   if ((x && !aligned16(x)) || (q && ((uintptr_t)q & 7) != 0))
     return fail(H3_EINVAL, "x must be 16-byte and q 8-byte aligned");

@@ -136,6 +136,20 @@ def test_invalid_shapes_rejected_on_host(lib, mutate, code):
                                   B.H3_WS_BLOCK) == 0
 
 
+def test_quantize_rows_validates_before_launch(lib):
+    """Bad widths, missing buffers and launches too large for one grid are
+    refused on the host (no GPU is touched)."""
+    rc = lib.h3_quantize_rows(None, 4, 100, 0, None, None, None)
+    assert rc == B.H3_EINVAL and "multiples of 8" in B.last_error()
+    rc = lib.h3_quantize_rows(None, 4, 1024, 256, None, None, None)
+    assert rc == B.H3_EINVAL and "required" in B.last_error()
+    rc = lib.h3_quantize_rows(None, 2 ** 30, 1024, 1024, None, None, None)
+    assert rc == B.H3_EUNSUPPORTED
+    rc = lib.h3_quantize_rows(None, 2 ** 26, 2 ** 20, 8, None, None, None)
+    assert rc == B.H3_EUNSUPPORTED and "too many" in B.last_error()
+    assert lib.h3_quantize_rows(None, 0, 1024, 0, None, None, None) == B.H3_OK  # nothing to do
+
+
 def test_entry_points_validate_before_launch(lib):
     """Null or undersized arguments are refused with an error code; nothing is
     launched (this runs without a GPU)."""
