@@ -104,36 +104,63 @@ __global__ __launch_bounds__(256) void k_modnorm(const bf16_t* __restrict__ x,
 }
 
 // vel[r][c] = sum_k z[r][k] * w[c][k] + b[c], fp32 with no rounding (h3.c
-// README: bf16 heads, F32 rows).  One wave per (row, group of 4 outputs): the
-// lanes split k, products are summed in fp32 and reduced across the wave.
+// README: bf16 heads, F32 rows), on the matrix cores: a workgroup takes 32
+// rows and all C outputs (CB blocks of 16, the last clamped); its 4 waves
+// split k into quarters, each summing its quarter with
+// v_mfma_f32_16x16x32_bf16 (fp32 sums), and the 4 partial sums of an output
+// are added in wave order through LDS before the bias.  z and w are read with
+// 16-byte loads straight into the operand registers (w, at most 256 rows, is
+// served from the caches).
+template <int CB>
 __global__ __launch_bounds__(256) void k_out_head(const bf16_t* __restrict__ z, int rows, int H,
                                                   const bf16_t* __restrict__ w,
                                                   const bf16_t* __restrict__ b, int C,
                                                   float* __restrict__ vel) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int cg = (C + 3) >> 2;
-  const int row = gw / cg, c0 = (gw % cg) * 4;
-  if (row >= rows) return;
-  const u32x4_t* zr = reinterpret_cast<const u32x4_t*>(z + (size_t)row * H);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int kv = lane; kv < (H >> 3); kv += 64) {
-    const u32x4_t zv = zr[kv];
+  extern __shared__ __attribute__((aligned(16))) float sPart[];  // [4][32][CB * 16]
+  constexpr int NC = CB * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+  const int r0 = blockIdx.x * 32;
+  const int kq = H / 4, k0 = wave * kq;  // this wave's quarter of k (a multiple of 64)
+  const bf16_t* zr[2];
+  const bf16_t* wr[CB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = min(c0 + j, C - 1);
-      const u32x4_t wv = reinterpret_cast<const u32x4_t*>(w + (size_t)c * H)[kv];
+  for (int i = 0; i < 2; ++i) zr[i] = z + (size_t)min(r0 + 16 * i + l16, rows - 1) * H + k0 + 8 * q4;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        acc[j] = fmaf(bflo(zv[t]), bflo(wv[t]), acc[j]);
-        acc[j] = fmaf(bfhi(zv[t]), bfhi(wv[t]), acc[j]);
-      }
-    }
+  for (int j = 0; j < CB; ++j) wr[j] = w + (size_t)min(16 * j + l16, C - 1) * H + k0 + 8 * q4;
+  // lane l of block (i, j): z row 16 i + 4 (l / 16) + e, output 16 j + l % 16
+  f32x4_t acc[2][CB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < kq; ks += 32) {
+    u32x4_t a[2], bw[CB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(zr[i] + ks);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) bw[j] = *reinterpret_cast<const u32x4_t*>(wr[j] + ks);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i]), as_bf16x8(bw[j]),
+                                                            acc[i][j], 0, 0, 0);
   }
+  float* const mine = sPart + wave * 32 * NC;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float s = wave_sum(acc[j]);
-    if (lane == 0 && c0 + j < C) vel[(size_t)row * C + c0 + j] = s + bf2f(b[c0 + j]);
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine[(16 * i + 4 * q4 + e) * NC + 16 * j + l16] = acc[i][j][e];
+  __syncthreads();
+  for (int idx = tid; idx < 32 * C; idx += 256) {
+    const int r = idx / C, c = idx % C;
+    if (r0 + r >= rows) break;  // idx grows with r
+    float s = sPart[r * NC + c];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) s += sPart[q * 32 * NC + r * NC + c];
+    vel[(size_t)(r0 + r) * C + c] = s + bf2f(b[c]);
   }
 }
 
@@ -170,9 +197,19 @@ hipError_t launch_modnorm(const bf16_t* x, bf16_t* out, int out_row0, const floa
 hipError_t launch_out_head(const bf16_t* z, int rows, int H, const bf16_t* w, const bf16_t* b,
                            int C, float* vel, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const long waves = (long)rows * ((C + 3) / 4);
-  hipLaunchKernelGGL(k_out_head, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, z, rows, H,
-                     w, b, C, vel);
+  if (C < 1 || C > 256 || H % 256 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((rows + 31) / 32)), block(256);
+  auto go = [&](auto kern, int cb) {
+    hipLaunchKernelGGL(kern, grid, block, (size_t)4 * 32 * cb * 16 * sizeof(float), s, z, rows,
+                       H, w, b, C, vel);
+  };
+  const int cb = (C + 15) / 16;
+  if (cb <= 2) go(k_out_head<2>, 2);
+  else if (cb <= 4) go(k_out_head<4>, 4);
+  else if (cb <= 6) go(k_out_head<6>, 6);
+  else if (cb <= 8) go(k_out_head<8>, 8);
+  else if (cb <= 12) go(k_out_head<12>, 12);
+  else go(k_out_head<16>, 16);
   return hipGetLastError();
 }
 
