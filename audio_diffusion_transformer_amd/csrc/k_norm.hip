@@ -3,8 +3,8 @@
 // Norm: h3.c README (fused gated AdaLN: one row kept on chip, per-row RMS,
 // rounded bf16 output) and TensorFold PR #949, "What it adds" (modulated
 // norm, final norm, rows out).  The row is read once with 16-byte loads held
-// in registers, the fp32 sum of squares is reduced across the wave, and the
-// output is written once: 2 x H x 2 bytes of HBM traffic per row.
+// in registers, the fp32 sum of squares is reduced across the workgroup, and
+// the output is written once: 2 x H x 2 bytes of HBM traffic per row.
 //
 //   out[r][c] = bf( x[r][c] * (sum_c x[r][c]^2 / H + eps)^-1/2 * (1 + scale[seg][c]) + shift[seg][c] )
 #include "common.h"
@@ -14,91 +14,99 @@ namespace h3 {
 
 namespace {
 
-// One wave per RW consecutive rows: each lane holds its NV 16-byte vectors
-// (columns 8c .. 8c+7, c = lane + 64 i) of every row in registers, so the
-// row is read once; the fp32 shift and scale of a column (64 bytes per 16
-// bytes of x) are read once for all RW rows, which share their segment except
-// where a segment ends inside the group (then a row reads its own).  Per
-// element the arithmetic is that of one row at a time: the lane's sum of
-// squares in column order, the wave sum, then the modulated value.  Two rows
-// per wave: 4 rows (half the occupancy) and the parameters staged in LDS per
-// workgroup (a 40 KB load before the first row) were both slower.
-template <int NV, int RW>
-__global__ __launch_bounds__(256) void k_modnorm(const bf16_t* __restrict__ x,
-                                                 bf16_t* __restrict__ out, int out_row0,
-                                                 const float* __restrict__ shift,
-                                                 const float* __restrict__ scale,
-                                                 int seg_stride, int row0, int row1, int H,
-                                                 int n_text, int n_prefix, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int rbase = row0 + (blockIdx.x * 4 + (threadIdx.x >> 6)) * RW;
-  if (rbase >= row1) return;
-  const int nvec = H >> 3;
-  u32x4_t v[RW][NV];
-  float rinv[RW];
-  int sg[RW];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int row = rbase + r;
-    float ss = 0.f;
-    if (row < row1) {
-      const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)row * H);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nvec) {
-          v[r][i] = xr[c];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float a = bflo(v[r][i][t]), b = bfhi(v[r][i][t]);
-            ss = fmaf(a, a, ss);
-            ss = fmaf(b, b, ss);
-          }
-        }
-      }
+// Column-split form: a workgroup of ceil(H / 512) waves takes a run of
+// consecutive rows; wave w owns columns 512 w .. 512 w + 511 (8 a lane) and
+// keeps their shift and scale (fp32) in registers for all of its rows,
+// reloading them only where a segment ends inside the run, so the parameters
+// are read once per workgroup instead of once per row.  Rows go kMnBatch at
+// a time: a lane's sum of squares of its 8 values (column order), the wave's
+// xor tree, then the waves' partial sums added in wave order through LDS.
+constexpr int kMnBatch = 4;   // rows per batch (8 held twice the registers: 4 waves per SIMD)
+constexpr int kMnRows = 32;  // rows per workgroup
+
+__global__ __launch_bounds__(1024) void k_modnorm_cols(const bf16_t* __restrict__ x,
+                                                       bf16_t* __restrict__ out, int out_row0,
+                                                       const float* __restrict__ shift,
+                                                       const float* __restrict__ scale,
+                                                       int seg_stride, int row0, int row1, int H,
+                                                       int n_text, int n_prefix, float eps,
+                                                       int rows_per_wg) {
+  __shared__ float part[2][kMnBatch][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int c8 = 512 * wave + 8 * lane;  // this lane's first column
+  const bool cok = c8 < H;
+  const int rb = row0 + blockIdx.x * rows_per_wg;
+  if (rb >= row1) return;  // uniform over the workgroup
+  const int re = min(rb + rows_per_wg, row1);
+  float shv[8], scv[8];
+  int cur = -1;
+  auto params = [&](int seg) {
+    const float* sh = shift + (size_t)seg * seg_stride + c8;
+    const float* sc = scale + (size_t)seg * seg_stride + c8;
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, k0 = s0, k1 = s0;
+    if (cok) {
+      s0 = *reinterpret_cast<const f32x4_t*>(sh);
+      s1 = *reinterpret_cast<const f32x4_t*>(sh + 4);
+      k0 = *reinterpret_cast<const f32x4_t*>(sc);
+      k1 = *reinterpret_cast<const f32x4_t*>(sc + 4);
     }
-    ss = wave_sum(ss);
-    rinv[r] = rsqrtf(ss / (float)H + eps);
-    sg[r] = row < n_text ? 0 : (row < n_prefix ? 1 : 2);
-  }
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= nvec) continue;
-    float shv[8], scv[8];
-    auto params = [&](int seg) {
-      const float* sh = shift + (size_t)seg * seg_stride + 8 * c;
-      const float* sc = scale + (size_t)seg * seg_stride + 8 * c;
-      const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sh);
-      const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(sh + 4);
-      const f32x4_t k0 = *reinterpret_cast<const f32x4_t*>(sc);
-      const f32x4_t k1 = *reinterpret_cast<const f32x4_t*>(sc + 4);
+    for (int e = 0; e < 4; ++e) {
+      shv[e] = s0[e];
+      shv[4 + e] = s1[e];
+      scv[e] = k0[e];
+      scv[4 + e] = k1[e];
+    }
+  };
+  int buf = 0;
+  for (int r = rb; r < re; r += kMnBatch, buf ^= 1) {
+    u32x4_t v[kMnBatch];
+    float ss[kMnBatch];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        shv[e] = s0[e];
-        shv[4 + e] = s1[e];
-        scv[e] = k0[e];
-        scv[4 + e] = k1[e];
+    for (int k = 0; k < kMnBatch; ++k) {
+      v[k] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (r + k < re && cok) v[k] = *reinterpret_cast<const u32x4_t*>(x + (size_t)(r + k) * H + c8);
+    }
+#pragma unroll
+    for (int k = 0; k < kMnBatch; ++k) {
+      float q = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float a = bflo(v[k][t]), b = bfhi(v[k][t]);
+        q = fmaf(a, a, q);
+        q = fmaf(b, b, q);
       }
-    };
-    params(sg[0]);
-    int cur = sg[0];
+      ss[k] = q;
+    }
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const int row = rbase + r;
-      if (row >= row1) break;
-      if (sg[r] != cur) {  // a segment ends inside this wave's rows
-        params(sg[r]);
-        cur = sg[r];
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int k = 0; k < kMnBatch; ++k) ss[k] += __shfl_xor(ss[k], o, kWave);
+    if (lane == 0)
+#pragma unroll
+      for (int k = 0; k < kMnBatch; ++k) part[buf][k][wave] = ss[k];
+    __syncthreads();  // (two buffers: the next batch's partial sums go to the other one)
+#pragma unroll
+    for (int k = 0; k < kMnBatch; ++k) {
+      const int row = r + k;
+      if (row >= re) break;
+      float tot = 0.f;
+      for (int q = 0; q < nw; ++q) tot += part[buf][k][q];
+      const float rinv = rsqrtf(tot / (float)H + eps);
+      const int seg = row < n_text ? 0 : (row < n_prefix ? 1 : 2);
+      if (seg != cur) {
+        params(seg);
+        cur = seg;
       }
+      if (!cok) continue;
       u32x4_t o;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float a = bflo(v[r][i][t]) * rinv[r], b = bfhi(v[r][i][t]) * rinv[r];
+        const float a = bflo(v[k][t]) * rinv, b = bfhi(v[k][t]) * rinv;
         o[t] = pack2(fmaf(a, 1.0f + scv[2 * t], shv[2 * t]),
                      fmaf(b, 1.0f + scv[2 * t + 1], shv[2 * t + 1]));
       }
-      reinterpret_cast<u32x4_t*>(out + (size_t)(row - out_row0) * H)[c] = o;
+      *reinterpret_cast<u32x4_t*>(out + (size_t)(row - out_row0) * H + c8) = o;
     }
   }
 }
@@ -179,18 +187,11 @@ hipError_t launch_modnorm(const bf16_t* x, bf16_t* out, int out_row0, const floa
                           int n_text, int n_prefix, float eps, hipStream_t s) {
   const int n = row1 - row0;
   if (n <= 0) return hipSuccess;
-  // vectors per lane: the row's H / 8 16-byte vectors over 64 lanes (H <= 8192)
-  const int nv = (H / 8 + 63) / 64;
-  auto go = [&](auto kern, int rw) {
-    const int waves = (n + rw - 1) / rw;
-    hipLaunchKernelGGL(kern, dim3((waves + 3) / 4), dim3(256), 0, s, x, out, out_row0, shift,
-                       scale, seg_stride, row0, row1, H, n_text, n_prefix, eps);
-  };
-  if (nv <= 2) go(k_modnorm<2, 2>, 2);
-  else if (nv <= 4) go(k_modnorm<4, 2>, 2);
-  else if (nv <= 8) go(k_modnorm<8, 2>, 2);
-  else if (nv <= 11) go(k_modnorm<11, 2>, 2);
-  else go(k_modnorm<16, 2>, 2);
+  if (H % 8 != 0 || H > 8192) return hipErrorInvalidValue;  // at most 16 waves of 512 columns
+  const int nw = (H + 511) / 512;
+  hipLaunchKernelGGL(k_modnorm_cols, dim3((n + kMnRows - 1) / kMnRows), dim3(64 * nw), 0, s, x,
+                     out, out_row0, shift, scale, seg_stride, row0, row1, H, n_text, n_prefix, eps,
+                     kMnRows);
   return hipGetLastError();
 }
 
