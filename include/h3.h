@@ -57,7 +57,8 @@ enum {
   H3_EWORKSPACE = -2,   /* ws_bytes smaller than h3_workspace_bytes() */
   H3_EHIP = -3,         /* a HIP launch or runtime error */
   H3_EUNSUPPORTED = -4  /* valid but not supported: head_dim not 64/128, more than 2048 tiles,
-                           more than 512 selected tiles, padded rows above 131072 */
+                           more than 512 selected tiles, padded rows above 131072, more than
+                           2^26 rows */
 };
 
 enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2, H3_WS_DIT_I8 = 3 };
@@ -65,7 +66,7 @@ enum { H3_WS_BLOCK = 0, H3_WS_DIT = 1, H3_WS_ATTN = 2, H3_WS_DIT_I8 = 3 };
 #define H3_ABI_VERSION 5
 
 typedef struct {
-  int32_t n_text, n_audio, n_video;  /* packed in this order */
+  int32_t n_text, n_audio, n_video;  /* packed in this order; >= 0, at most 2^26 in all */
   int32_t hidden;                    /* H: multiple of 256, <= 8192 */
   int32_t n_heads, head_dim;         /* head_dim in {64, 128}; attention width A = n_heads * head_dim
                                         (may differ from H; (3 + gate) A a multiple of 256) */
