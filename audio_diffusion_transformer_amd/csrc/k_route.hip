@@ -40,10 +40,10 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 // PL: scores held per lane (tiles <= 64 PL)
-// (up to 4 scores per lane: at most 80 VGPRs, six waves per SIMD, so three
+// (up to 8 scores per lane: at most 80 VGPRs, six waves per SIMD, so three
 // 8-wave workgroups share a CU)
 template <int D, int PL>
-__global__ __launch_bounds__(64 * kQT, PL <= 4 ? 6 : 1) void k_route(RouteArgs a) {
+__global__ __launch_bounds__(64 * kQT, PL <= 8 ? 6 : 1) void k_route(RouteArgs a) {
   constexpr int SR = D + 4;  // LDS row stride (floats): 16-byte row reads of 16 lanes hit distinct banks
   __shared__ __attribute__((aligned(16))) float sRow[64 * SR];
   __shared__ __attribute__((aligned(16))) float sQ[kQT][D];
@@ -100,7 +100,10 @@ __global__ __launch_bounds__(64 * kQT, PL <= 4 ? 6 : 1) void k_route(RouteArgs a
       if (active && j < nT) {
         const float* kr = &sRow[lane * SR];
         float s = 0.f;
-#pragma unroll 2  // (deeper unrolling holds more loads in flight but costs occupancy)
+        // (deeper unrolling holds more loads in flight but costs registers: by 2
+        // up to 4 scores per lane, not at all with 8, for the 80-register bound)
+        constexpr int kScoreUnroll = PL <= 4 ? 2 : 1;
+#pragma unroll kScoreUnroll
         for (int c4 = 0; c4 < D / 4; ++c4) {
           const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kr + 4 * c4);
           const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(&sQ[wave][4 * c4]);
