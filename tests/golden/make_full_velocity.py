@@ -1,8 +1,14 @@
-"""Writes full_velocity_2block.json: the oracle's velocities of a two-block
-forward at the full size (15,435 rows: 512 text / 543 audio / 14,380 video,
-hidden 5,120, 40 x 128 heads, GELU FFN 20,480, tile 64, top-k 32 + pooled)
-on sampled audio and video rows, and the oracle's self-noise floor on the same
-rows.
+"""Writes the oracle's velocities of a two-block forward at full size on
+sampled audio and video rows, and the oracle's self-noise floor on the same
+rows, for two workloads:
+
+- full_velocity_2block.json: 15,435 rows (512 text / 543 audio / 14,380
+  video), hidden 5,120, 40 x 128 heads, GELU FFN 20,480, tile 64, top-k 32
+  + pooled;
+- fasth3_velocity_2block.json: the pages' FastH3 block and geometry, 15,435
+  rows (36 text / 414 audio / 14,985 video in 4 x 4 x 4 cubes of a 37 x 15 x
+  27 grid), hidden 5,376, 56 x 128 heads (attention width 7,168), SwiGLU FFN
+  14,336, the routing gate, top-k 56 + pooled.
 
 Calls only oracle/ (the plain C++ oracle) and the seeded input generator.  The
 GPU test tests/test_gpu_velocity.py regenerates the same inputs and compares
@@ -14,7 +20,8 @@ sampled rows; then the final norm and the heads on those rows (the pages'
 first-forward velocity comparison, "TensorFold PR #949", Receipts: Parity).
 Self-noise: the same computation with the tile-mean and tile-score sums
 reversed (the pages' self-noise rows of the same table), compared with the
-forward one.  Run: python tests/golden/make_full_velocity.py  (a few minutes).
+forward one.  Run: python tests/golden/make_full_velocity.py [full|fasth3]
+(a few minutes each).
 """
 from __future__ import annotations
 
@@ -32,14 +39,25 @@ sys.path.insert(0, ROOT)
 from audio_diffusion_transformer_amd import synth as S  # noqa: E402
 from oracle import h3_ref as C  # noqa: E402
 
-OUT = os.path.join(HERE, "full_velocity_2block.json")
 L = 2
 SEED = 42
+WORKLOADS = {
+    "full": (S.FULL, "full_velocity_2block.json",
+             "15,435 rows (512/543/14,380), hidden 5120, 40x128 heads, GELU FFN 20480, "
+             "tile 64, top-k 32 + pooled"),
+    "fasth3": (S.FASTH3, "fasth3_velocity_2block.json",
+               "15,435 rows (36/414/14,985, 4x4x4 cubes of a 37x15x27 grid), hidden 5376, "
+               "56x128 heads, SwiGLU FFN 14336, routing gate, top-k 56 + pooled"),
+}
 
 
-def inputs():
+def golden_path(workload="full"):
+    return os.path.join(HERE, WORKLOADS[workload][1])
+
+
+def inputs(workload="full"):
     """The two-block forward's inputs (also used by the GPU test)."""
-    sh = S.FULL
+    sh = WORKLOADS[workload][0]
     ts, npt = S.tile_map(sh)
     blocks = [S.block_weights(sh, seed=SEED + l) for l in range(L)]
     mods = np.stack([S.modulation(sh, block=l, seed=SEED) for l in range(L)])
@@ -80,9 +98,9 @@ def _metrics(got, ref):
                 max_abs=float(np.max(np.abs(g - r))))
 
 
-def main():
+def main(workload="full"):
     t0 = time.time()
-    sh, ts, npt, blocks, mods, head, mf, rope, x = inputs()
+    sh, ts, npt, blocks, mods, head, mf, rope, x = inputs(workload)
     aud, vid = sample_rows(sh, ts)
     rows = np.concatenate([aud, vid])
     vv, va = oracle_velocities(sh, ts, npt, blocks, mods, head, mf, rope, x, rows, 0)
@@ -91,18 +109,18 @@ def main():
                                    C.REV_MEANS | C.REV_SCORES)
     out = dict(
         description="Oracle (plain C++, fp32 ascending sums) velocities of a 2-block forward at "
-                    "15,435 rows (512/543/14,380), hidden 5120, 40x128 heads, GELU FFN 20480, "
-                    "tile 64, top-k 32 + pooled, seed 42, x with the smooth field; written by "
-                    "tests/golden/make_full_velocity.py",
+                    + WORKLOADS[workload][2] + ", seed 42, x with the smooth field; written by "
+                    "tests/golden/make_full_velocity.py " + workload,
         audio_rows=aud.tolist(), video_rows=vid.tolist(),
         vel_audio=[[float(np.float32(v)) for v in r] for r in va],
         vel_video=[[float(np.float32(v)) for v in r] for r in vv],
         self_noise=dict(audio=_metrics(va_r, va), video=_metrics(vv_r, vv)),
         oracle_seconds=round(t1 - t0, 1), threads=C.set_threads(0))
-    with open(OUT, "w") as f:
+    path = golden_path(workload)
+    with open(path, "w") as f:
         json.dump(out, f, indent=0)
-    print("wrote", OUT, "self-noise", out["self_noise"], "oracle s", out["oracle_seconds"])
+    print("wrote", path, "self-noise", out["self_noise"], "oracle s", out["oracle_seconds"])
 
 
 if __name__ == "__main__":
-    main()
+    main(*sys.argv[1:2])

@@ -1,12 +1,18 @@
 """Velocity parity at the full size: h3_dit_forward with two blocks at 15,435
-rows (512 text / 543 audio / 14,380 video, hidden 5,120, 40 x 128 heads, GELU
-FFN 20,480, tile 64, top-k 32 + pooled) against the oracle's velocities of the
-sampled rows stored in tests/golden/full_velocity_2block.json (written by
-tests/golden/make_full_velocity.py from the plain C++ oracle on the same seeded
-inputs).  Bar: the acceptance bar, cos >= 0.998 and relative L2 <= 0.06, per
-output head; the oracle's own self-noise floor (reversed tile sums) on the same
-rows is printed beside the GPU's error (TensorFold PR #949, Receipts: Parity,
-the first forward's velocities and the self-noise rows)."""
+rows against the oracle's velocities of sampled rows, stored in tests/golden/
+(written by tests/golden/make_full_velocity.py from the plain C++ oracle on
+the same seeded inputs), for two workloads:
+
+- full: 512 text / 543 audio / 14,380 video rows, hidden 5,120, 40 x 128
+  heads, GELU FFN 20,480, tile 64, top-k 32 + pooled;
+- fasth3: the pages' block and geometry (36 / 414 / 14,985 rows, video in
+  4 x 4 x 4 cubes, hidden 5,376, 56 x 128 heads, SwiGLU FFN 14,336, the
+  routing gate, top-k 56 + pooled).
+
+Bar: the acceptance bar, cos >= 0.998 and relative L2 <= 0.06, per output
+head; the oracle's own self-noise floor (reversed tile sums) on the same rows
+is printed beside the GPU's error (TensorFold PR #949, Receipts: Parity, the
+first forward's velocities and the self-noise rows)."""
 import json
 import os
 import sys
@@ -26,11 +32,12 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 sys.path.insert(0, GOLDEN)
 
 
-def test_full_size_two_block_velocities():
+@pytest.mark.parametrize("workload", ["full", "fasth3"])
+def test_full_size_two_block_velocities(workload):
     import make_full_velocity as MF
-    print("case: h3_dit_forward, 2 blocks at 15,435 rows (full size), sampled rows", flush=True)
-    ref = json.load(open(os.path.join(GOLDEN, "full_velocity_2block.json")))
-    sh, ts, npt, blocks, mods, head, mf, rope, x = MF.inputs()
+    print(f"case: h3_dit_forward, 2 blocks at 15,435 rows ({workload}), sampled rows", flush=True)
+    ref = json.load(open(MF.golden_path(workload)))
+    sh, ts, npt, blocks, mods, head, mf, rope, x = MF.inputs(workload)
     aud, vid = MF.sample_rows(sh, ts)
     assert aud.tolist() == ref["audio_rows"] and vid.tolist() == ref["video_rows"]
     shape = B.make_shape(sh, ts, npt)
